@@ -1,0 +1,215 @@
+"""Benchmark: tree-verify steps/sec and tree-attention HBM GB/s on one MI355X.
+
+Workload (default): LLaMA2-13B-shaped verification step, batch 1 -- draft tree
+of depth 6, top-k 10, m 10, Rerank to 60 nodes (T = 61 rows), vocab 32000;
+tree attention through 40 layers of 40 heads x 128 with a bf16 KV cache at
+context 4096 (40 distinct layer buffers, 3.46 GB, so nothing stays in the
+256 MB last-level cache between layers); sampled verification at temperature 1
+with Philox uniforms.  Inputs are seeded synthetic tensors of that shape.
+
+One step = eagle_tree_expand x 6 + eagle_tree_rerank + eagle_tree_mask +
+eagle_tree_attention x 40 + eagle_verify, enqueued on one stream.  Inputs are
+resident in HBM before timing starts.
+
+The JSON line carries:
+  value     steps/s (whole job, one GPU)
+  roofline  tree-attention HBM bandwidth: algorithmic bytes per launch (K + V of
+            the ctx + T rows of every KV head, plus Q and O) / average launch
+            time measured with HIP events on the launch stream, against the
+            8 TB/s HBM peak
+  cpu_baseline  the CPU oracle on a bounded sample (tree + 1 attention layer +
+            verify, single thread), scaled to one full step
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attn_llama2_13b_traffic.json")
+
+
+def attention_bytes_per_launch(w) -> int:
+    """K + V over ctx + T rows per KV head, plus Q and O (bf16)."""
+    elt = 4 if w.dtype == "f32" else 2
+    kv = 0
+    for c in w.ctx_lens():
+        kv += 2 * w.n_kv_heads * (int(c) + w.T) * w.head_dim * elt
+    qo = 2 * w.batch * w.T * w.n_q_heads * w.head_dim * elt
+    return kv + qo
+
+
+def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed):
+    """Oracle timing on a bounded sample: full tree + one attention layer + one
+    verification, single-threaded, scaled to the full step (layers x layer time)."""
+    import oracle
+    from draft_tree_verification_eagle_amd import workload as wl
+    import torch
+
+    b = 0
+    t0 = time.perf_counter()
+    tree, kept, flat = oracle.build_tree(vs_draft[b], int(vs_root[b]), w.depth, w.topk, w.m, w.n, w.ctx)
+    t_tree = time.perf_counter() - t0
+    q, k, v, off, total = wl.attention_inputs(w, 0, device="cpu")
+    qf = q[0].float().numpy(); kf = k.float().numpy(); vf = v.float().numpy()
+    t0 = time.perf_counter()
+    oracle.attention(qf, kf, vf, flat["mask"], w.ctx)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    if temperature > 0:
+        oracle.verify_sampled(target[b], flat["flat_token"], flat["flat_parent"], w.depth, temperature, seed, 0, 0)
+    else:
+        oracle.verify_greedy(target[b], flat["flat_token"], flat["flat_parent"], w.depth)
+    t_verify = time.perf_counter() - t0
+    t_step = t_tree + w.layers * t_layer + t_verify
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"tree build + 1 of {w.layers} attention layers (fp64) + 1 verification, one thread; "
+                      f"step time = tree {t_tree:.3f}s + {w.layers} x layer {t_layer:.2f}s + verify {t_verify:.3f}s",
+            "oracle_attention_GBps": attention_bytes_per_launch(w) / t_layer / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama2_13b")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from draft_tree_verification_eagle_amd import step as stepm
+    from draft_tree_verification_eagle_amd import workload as wl
+
+    w = wl.CONFIGS[args.config]
+    temperature = w.temperatures[-1]
+    seed = 12345
+    torch.cuda.set_device(0)
+    print(f"[bench] allocating {args.config} inputs", file=sys.stderr, flush=True)
+    vs = stepm.VerifyStep(w, device="cuda:0", with_lse=False)
+    # target logits depend on the tree: build it once (untimed), plant, upload
+    vs.tree()
+    torch.cuda.synchronize()
+    ft, fp = vs.flat_host()
+    target = wl.plant(wl.target_logits_base(w), ft, fp, w.plant_frac, w.seed)
+    vs.set_target(target)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_attn = vs.n_layers
+    graph = None
+    if args.graph:
+        for i in range(3):
+            vs.run(temperature, seed, i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            vs.run(temperature, seed, 0)
+        torch.cuda.synchronize()
+
+    def one_step(i, ev=None):
+        if graph is not None:
+            graph.replay()
+            return
+        vs.tree()
+        if ev is not None:
+            ev[0].record(stream)
+        vs.attention()
+        if ev is not None:
+            ev[1].record(stream)
+        vs.verify(temperature, seed, i)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        one_step(i, None if graph is not None else evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.3f}s)", file=sys.stderr, flush=True)
+
+    # attention launch time: events around the 40 launches of each timed step
+    if graph is None:
+        attn_ms = [a.elapsed_time(b) for a, b in evs]
+        ms_per_launch = float(np.median(attn_ms)) / n_attn
+    else:
+        # graph mode: time the attention launches alone on the same stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            vs.attention()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_launch = e0.elapsed_time(e1) / (5 * n_attn)
+    bytes_launch = attention_bytes_per_launch(w)
+    achieved = bytes_launch / (ms_per_launch * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            traffic = json.load(open(TRAFFIC_FILE)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "tree-verify steps/sec + tree-attn HBM GB/s (% peak), 13B shape ctx 4096, 60 nodes",
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: draft tree d{w.depth} k{w.topk} m{w.m} n{w.n} (T={w.T}), vocab {w.vocab}, "
+                        f"tree attention {w.layers} layers x {w.n_q_heads}q/{w.n_kv_heads}kv heads x {w.head_dim}, "
+                        f"{w.dtype} KV at ctx {w.ctx}, verify temperature {temperature}",
+            "batch": w.batch, "ctx_len": w.ctx, "tree_rows": w.T, "layers": w.layers,
+            "graph": bool(args.graph), "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "tree_attn_bf16_kernel",
+            "bytes_per_launch": bytes_launch,
+            "us_per_launch": round(ms_per_launch * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, vs.draft_np, vs.root_np, target, temperature, seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+// C ABI of the tree-verification library: host-side validation, then launches on
+// the caller's stream.  See include/eagle_tree.h for the contract of each call.
+#include <math.h>
+
+#include "launchers.hpp"
+
+namespace {
+
+using eagle::attention_max_batch;
+
+bool tree_cfg_ok(const eagle_tree_cfg* c) {
+    return c && c->batch >= 0 && c->batch <= EAGLE_MAX_BATCH && c->vocab >= 1 && c->depth >= 1 &&
+           c->topk >= 1 && c->m >= 1 && c->n >= 0 && c->topk <= c->vocab;
+}
+
+// Tree shape implied by the cfg; false if it exceeds this build's limits.
+bool tree_shape(const eagle_tree_cfg* c, int32_t* capacity) {
+    int64_t f = 1, cap = 1;
+    for (int l = 0; l < c->depth; ++l) {
+        cap += f * c->topk;
+        if (cap > EAGLE_MAX_CAPACITY) return false;
+        f = f * c->topk < c->m ? f * c->topk : c->m;
+    }
+    *capacity = (int32_t)cap;
+    return true;
+}
+
+int tree_limits(const eagle_tree_cfg* c, int32_t* cap) {
+    if (!tree_cfg_ok(c)) return EAGLE_ERR_INVALID_ARG;
+    if (c->topk > EAGLE_MAX_TOPK || c->depth > 255 || (int64_t)c->m * c->topk > EAGLE_MAX_LAYER_NODES ||
+        c->n + 1 > EAGLE_MAX_TREE_ROWS || !tree_shape(c, cap))
+        return EAGLE_ERR_UNSUPPORTED;
+    if (c->n > *cap - 1) return EAGLE_ERR_INVALID_ARG;
+    return EAGLE_OK;
+}
+
+bool state_ok(const eagle_tree_state* s) {
+    return s && s->token && s->parent && s->depth && s->value && s->frontier && s->n_nodes;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t eagle_tree_capacity(const eagle_tree_cfg* cfg) {
+    int32_t cap = 0;
+    if (!tree_cfg_ok(cfg) || !tree_shape(cfg, &cap)) return -1;
+    return cap;
+}
+
+int32_t eagle_tree_frontier_rows(const eagle_tree_cfg* cfg, int32_t layer) {
+    if (!tree_cfg_ok(cfg) || layer < 1 || layer > cfg->depth) return -1;
+    int64_t f = 1;
+    for (int l = 1; l < layer; ++l) f = f * cfg->topk < cfg->m ? f * cfg->topk : cfg->m;
+    return (int32_t)f;
+}
+
+int eagle_tree_expand(const eagle_tree_cfg* cfg, int32_t layer, const float* draft_logits,
+                      const int32_t* root_token, const eagle_tree_state* state, hipStream_t stream) {
+    int32_t cap = 0;
+    const int st = tree_limits(cfg, &cap);
+    if (st != EAGLE_OK) return st;
+    if (layer < 1 || layer > cfg->depth || !state_ok(state) || (layer == 1 && !root_token))
+        return EAGLE_ERR_INVALID_ARG;
+    if (cfg->batch == 0) return EAGLE_OK;
+    if (!draft_logits) return EAGLE_ERR_INVALID_ARG;
+    const int rows = eagle_tree_frontier_rows(cfg, layer);
+    return from_hip(eagle::launch_expand(*cfg, layer, rows, cap, draft_logits, root_token, *state, stream));
+}
+
+int eagle_tree_rerank(const eagle_tree_cfg* cfg, const eagle_tree_state* state, int32_t* kept,
+                      hipStream_t stream) {
+    int32_t cap = 0;
+    const int st = tree_limits(cfg, &cap);
+    if (st != EAGLE_OK) return st;
+    if (!state_ok(state) || (cfg->n > 0 && !kept)) return EAGLE_ERR_INVALID_ARG;
+    if (cfg->batch == 0 || cfg->n == 0) return EAGLE_OK;
+    return from_hip(eagle::launch_rerank(*cfg, cap, *state, kept, stream));
+}
+
+int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state, const int32_t* kept,
+                    const int32_t* ctx_len, int32_t* flat_token, int32_t* flat_parent,
+                    int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream) {
+    int32_t cap = 0;
+    const int st = tree_limits(cfg, &cap);
+    if (st != EAGLE_OK) return st;
+    if (!state_ok(state) || (cfg->n > 0 && !kept) || !ctx_len || !flat_token || !flat_parent ||
+        !flat_depth || !position || !mask)
+        return EAGLE_ERR_INVALID_ARG;
+    if (cfg->batch == 0) return EAGLE_OK;
+    return from_hip(eagle::launch_mask(*cfg, cap, *state, kept, ctx_len, flat_token, flat_parent,
+                                       flat_depth, position, mask, stream));
+}
+
+static int attn_desc_check(const eagle_attn_desc* d) {
+    if (!d || d->batch < 0 || d->T < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+        d->n_q_heads % d->n_kv_heads != 0 || d->kv_rows_total < (int64_t)d->batch * d->T ||
+        !(d->scale >= 0.0f) || isinf(d->scale))
+        return EAGLE_ERR_INVALID_ARG;
+    if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
+    if (d->T > EAGLE_MAX_TREE_ROWS) return EAGLE_ERR_UNSUPPORTED;
+    if (d->dtype == EAGLE_BF16 && (d->head_dim != 128 || d->batch > attention_max_batch()))
+        return EAGLE_ERR_UNSUPPORTED;
+    if (d->dtype == EAGLE_F32 && d->head_dim > 128) return EAGLE_ERR_UNSUPPORTED;
+    return EAGLE_OK;
+}
+
+size_t eagle_tree_attention_workspace(const eagle_attn_desc* desc) {
+    if (attn_desc_check(desc) != EAGLE_OK) return 0;
+    return eagle::attention_workspace_bytes(*desc);
+}
+
+int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void* k_cache,
+                         const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int st = attn_desc_check(desc);
+    if (st != EAGLE_OK) return st;
+    if (desc->batch == 0) return EAGLE_OK;
+    if (!q || !k_cache || !v_cache || !mask || !o || !desc->ctx_len || !desc->kv_row_off)
+        return EAGLE_ERR_INVALID_ARG;
+    const size_t need = eagle::attention_workspace_bytes(*desc);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return EAGLE_ERR_WORKSPACE;
+    return from_hip(eagle::launch_attention(*desc, q, k_cache, v_cache, mask, o, lse, workspace, stream));
+}
+
+size_t eagle_verify_workspace(const eagle_tree_cfg* cfg) {
+    int32_t cap = 0;
+    if (tree_limits(cfg, &cap) != EAGLE_OK) return 0;
+    return eagle::verify_workspace_bytes(*cfg);
+}
+
+int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const int32_t* flat_token,
+                 const int32_t* flat_parent, float temperature, uint64_t seed, uint64_t step,
+                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+    int32_t cap = 0;
+    const int st = tree_limits(cfg, &cap);
+    if (st != EAGLE_OK) return st;
+    if (!(temperature >= 0.0f) || isinf(temperature)) return EAGLE_ERR_INVALID_ARG;
+    if (cfg->batch == 0) return EAGLE_OK;
+    if (!target_logits || !flat_token || !flat_parent || !accept_len || !accept_path || !out_tokens)
+        return EAGLE_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < eagle::verify_workspace_bytes(*cfg)) return EAGLE_ERR_WORKSPACE;
+    return from_hip(eagle::launch_verify(*cfg, target_logits, flat_token, flat_parent, temperature, seed,
+                                         step, accept_len, accept_path, out_tokens, workspace, stream));
+}
+
+const char* eagle_status_string(int status) {
+    switch (status) {
+        case EAGLE_OK: return "ok";
+        case EAGLE_ERR_INVALID_ARG: return "invalid argument";
+        case EAGLE_ERR_UNSUPPORTED: return "unsupported by this build";
+        case EAGLE_ERR_WORKSPACE: return "workspace missing or too small";
+        case EAGLE_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Device helpers shared by the gfx950 kernels of the tree-verification library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eagle {
+
+constexpr int kWave = 64;
+
+// Order-preserving map of an fp32 value to uint32 (larger float -> larger key).
+// -0.0 is folded onto +0.0 so that equal floats give equal keys.
+__device__ __forceinline__ uint32_t float_order_key(float x) {
+    if (x == 0.0f) x = 0.0f;
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit key whose maximum is the larger logit, and among equal logits the lower
+// token id.
+__device__ __forceinline__ uint64_t logit_key(float z, uint32_t token) {
+    return ((uint64_t)float_order_key(z) << 32) | (uint64_t)(0xFFFFFFFFu - token);
+}
+__device__ __forceinline__ uint32_t logit_key_token(uint64_t key) {
+    return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, mask, kWave);
+    hi = __shfl_xor(hi, mask, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// Block-wide sum of one double per thread; every thread receives the total.
+// `scratch` needs blockDim.x / 64 doubles of LDS.  Contains __syncthreads.
+__device__ __forceinline__ double block_sum_f64(double v, double* scratch) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    v = wave_sum_f64(v);
+    if (lane == 0) scratch[wid] = v;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < nw; ++w) t += scratch[w];
+    __syncthreads();
+    return t;
+}
+
+// In-place bitonic sort of P (power of two) uint64 keys in LDS into DESCENDING
+// order, by all threads of the block.  Ends with __syncthreads.
+__device__ __forceinline__ void lds_bitonic_sort_desc(uint64_t* keys, int P) {
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (P >> 1); i += blockDim.x) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = keys[lo], b = keys[hi];
+                if ((a < b) == desc) { keys[lo] = b; keys[hi] = a; }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): the 4x32 S-box with its two
+// published multipliers, the key bumped by the two Weyl constants between the
+// ten rounds.
+// ---------------------------------------------------------------------------
+struct Philox4x32 {
+    uint32_t c0, c1, c2, c3;
+};
+
+__device__ __forceinline__ Philox4x32 philox4x32_10(Philox4x32 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint64_t a = (uint64_t)0xD2511F53u * c.c0;
+        const uint64_t b = (uint64_t)0xCD9E8D57u * c.c2;
+        Philox4x32 n;
+        n.c0 = (uint32_t)(b >> 32) ^ c.c1 ^ k0;
+        n.c1 = (uint32_t)b;
+        n.c2 = (uint32_t)(a >> 32) ^ c.c3 ^ k1;
+        n.c3 = (uint32_t)a;
+        c = n;
+    }
+    return c;
+}
+
+// Uniform in [0, 1) for one acceptance decision: key = the seed's two words,
+// counter = (slot, tree row, sequence, low word of the step); 24 top bits of
+// the first output word.
+__device__ __forceinline__ double decision_uniform(uint64_t seed, uint64_t step, uint32_t seq,
+                                                   uint32_t row, uint32_t slot) {
+    Philox4x32 c{slot, row, seq, (uint32_t)step};
+    Philox4x32 o = philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    return (double)(o.c0 >> 8) * (1.0 / 16777216.0);
+}
+
+constexpr uint32_t kBonusSlot = 0xFFFFFFFFu;
+
+}  // namespace eagle

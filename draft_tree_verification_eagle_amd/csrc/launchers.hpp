@@ -1,0 +1,38 @@
+// Internal host-side launch entry points of the tree-verification library.  The
+// C ABI (api.hip) validates arguments and then calls these; they only enqueue
+// kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "eagle_tree.h"
+
+namespace eagle {
+
+hipError_t launch_expand(const eagle_tree_cfg& cfg, int layer, int rows, int cap,
+                         const float* logits, const int32_t* root_token,
+                         const eagle_tree_state& st, hipStream_t stream);
+
+hipError_t launch_rerank(const eagle_tree_cfg& cfg, int cap, const eagle_tree_state& st,
+                         int32_t* kept, hipStream_t stream);
+
+hipError_t launch_mask(const eagle_tree_cfg& cfg, int cap, const eagle_tree_state& st,
+                       const int32_t* kept, const int32_t* ctx_len, int32_t* flat_token,
+                       int32_t* flat_parent, int32_t* flat_depth, int32_t* position,
+                       uint64_t* mask, hipStream_t stream);
+
+// Tree attention.  Workspace layout and launch shape are decided here.
+int attention_max_batch();
+size_t attention_workspace_bytes(const eagle_attn_desc& d);
+hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k,
+                            const void* v, const uint64_t* mask, void* o, float* lse,
+                            void* workspace, hipStream_t stream);
+
+size_t verify_workspace_bytes(const eagle_tree_cfg& cfg);
+hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const int32_t* flat_token,
+                         const int32_t* flat_parent, float temperature, uint64_t seed,
+                         uint64_t step, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* out_tokens, void* workspace, hipStream_t stream);
+
+}  // namespace eagle

@@ -1,0 +1,195 @@
+/*
+ * eagle_tree.h -- C ABI of the MI355X (gfx950) draft-tree verification library.
+ *
+ * One verification step of EAGLE-2 speculative sampling, as five calls:
+ *   eagle_tree_expand     grow the dynamic draft tree by one layer
+ *   eagle_tree_rerank     keep the n best nodes of the whole tree
+ *   eagle_tree_mask       flatten the kept tree: tokens, parents, positions, ancestor mask
+ *   eagle_tree_attention  tree attention of the flattened rows against the KV cache
+ *   eagle_verify          lossless acceptance (greedy or sampled) over target logits
+ *
+ * Pages defining the operations (cited by title and passage):
+ *   EAGLE-2 page -- news write-up of "EAGLE-2: Faster Inference of Language Models
+ *     with Dynamic Draft Trees": the passage on the two stages (node value =
+ *     product of confidences on the root path; Expand takes the m best nodes of the
+ *     last layer; Rerank keeps the n best of the whole tree, shallower first on equal
+ *     values so the kept tree stays connected) and the passage after it
+ *     (flattening to 1-D, ancestor-only attention mask -- the It / is / a / has
+ *     example -- and positions adjusted to match autoregressive decoding); its
+ *     opening paragraph (one target forward verifies the draft).
+ *   EAGLE page -- abstract of "EAGLE: Speculative Sampling Requires Rethinking
+ *     Feature Uncertainty": output distribution identical to vanilla decoding.
+ *   CSDN page -- "论文解读：eagle/eagle2", sections 1.1 and 1.2: verification keeps
+ *     the target's distribution, under greedy and under sampled decoding.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers owned by the caller; struct
+ *     arguments (eagle_tree_cfg, eagle_tree_state, eagle_attn_desc) are read on the
+ *     host during the call only.  The library never allocates or frees device
+ *     memory and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *   - Arguments are validated on the host first; on any failure the call returns
+ *     the status and launches nothing.  After launching, a launch error maps to
+ *     EAGLE_ERR_HIP.  Faults inside kernels surface at the caller's next sync.
+ *   - Logits containing NaN or Inf give unspecified (but memory-safe) results.
+ *   - Calls on distinct streams with distinct buffers are independent.
+ */
+#ifndef EAGLE_TREE_H
+#define EAGLE_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EAGLE_OK = 0,
+    EAGLE_ERR_INVALID_ARG = -1, /* null pointer, out-of-range size, inconsistent shape */
+    EAGLE_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits (below) */
+    EAGLE_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
+    EAGLE_ERR_HIP = -4          /* the HIP runtime reported a launch error */
+} eagle_status;
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+
+/* Limits of this build. */
+#define EAGLE_MAX_TREE_ROWS 64     /* T = n + 1: one 64-bit ancestor-mask word per row */
+#define EAGLE_MAX_TOPK 32          /* children per expanded node */
+#define EAGLE_MAX_LAYER_NODES 1024 /* m * topk: nodes created in one layer */
+#define EAGLE_MAX_CAPACITY 4096    /* tree nodes incl. the root after `depth` layers */
+#define EAGLE_MAX_BATCH 1024
+
+/* Tree parameters, identical for every sequence of the batch.
+ *   depth : draft layers below the root (>= 1); at most `depth` tokens are accepted
+ *   topk  : children given to each expanded node (its draft row's top-k tokens)
+ *   m     : nodes of the last layer expanded at the next layer
+ *   n     : nodes kept by Rerank, root excluded (the flattened tree has T = n + 1 rows) */
+typedef struct {
+    int32_t batch, vocab, depth, topk, m, n;
+} eagle_tree_cfg;
+
+/* Device-side tree, [batch][capacity] per array (capacity from eagle_tree_capacity).
+ * Node 0 of each sequence is the root (parent -1, depth 0, value 0).  Children are
+ * numbered in creation order: layer by layer, frontier order, then draft rank.
+ * value = sum of fp32 log-confidences on the root path.
+ * frontier [batch][m]: ids of the nodes whose draft rows the next layer consumes,
+ * best first (value desc, id asc).  n_nodes [batch]: nodes created so far. */
+typedef struct {
+    int32_t *token, *parent, *depth;
+    float *value;
+    int32_t *frontier, *n_nodes;
+} eagle_tree_state;
+
+/* Nodes after all `depth` layers: 1 + topk * sum_l F_l, F_1 = 1,
+ * F_{l+1} = min(m, F_l * topk).  Returns -1 for an invalid cfg. */
+int32_t eagle_tree_capacity(const eagle_tree_cfg* cfg);
+
+/* Draft-logit rows consumed at `layer` (1..depth) per sequence: F_layer.
+ * Returns -1 for an invalid cfg or layer. */
+int32_t eagle_tree_frontier_rows(const eagle_tree_cfg* cfg, int32_t layer);
+
+/* Expand (EAGLE-2 page, two-stage passage): for every frontier node f of every
+ * sequence, take its draft row z (fp32, [batch][F_layer][vocab], row j belongs to
+ * frontier[j]; at layer 1 the single row belongs to the root), and append its
+ * top-k tokens (logit desc, token id asc) as children with
+ *     logq  = (z_t - max z) - lse,   lse = log sum exp(z - max z)
+ *     value = value(f) + logq
+ * lse is summed in fp64 and rounded to fp32 once; logq and value are fp32
+ * subtraction / addition.  Then, when layer < depth, frontier := the
+ * min(m, |new layer|) new nodes of highest value (ties: lower id).
+ * Layer 1 (re)initialises the tree from root_token [batch] (read only then).
+ * Layers must be called in order 1..depth on the same stream. */
+int eagle_tree_expand(const eagle_tree_cfg* cfg, int32_t layer, const float* draft_logits,
+                      const int32_t* root_token, const eagle_tree_state* state,
+                      hipStream_t stream);
+
+/* Rerank (EAGLE-2 page, two-stage passage): per sequence, the n non-root nodes
+ * that come first in (value desc, depth asc, id asc), written to kept [batch][n]
+ * in ascending id order.  Requires all `depth` layers expanded.  n larger than
+ * the number of non-root nodes is EAGLE_ERR_INVALID_ARG. */
+int eagle_tree_rerank(const eagle_tree_cfg* cfg, const eagle_tree_state* state, int32_t* kept,
+                      hipStream_t stream);
+
+/* Flatten + mask + positions (EAGLE-2 page, passage after the two stages).
+ * Row 0 is the root, rows 1..n are the kept nodes in ascending id (a topological
+ * order).  Outputs, [batch][T] int32: flat_token, flat_parent (row index, -1 for
+ * the root), flat_depth, position = ctx_len[b] + depth; mask [batch][T] uint64:
+ * bit j of row i is set iff row j lies on the root-to-i path (i included).
+ * ctx_len [batch] int32 device. */
+int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
+                    const int32_t* kept, const int32_t* ctx_len, int32_t* flat_token,
+                    int32_t* flat_parent, int32_t* flat_depth, int32_t* position,
+                    uint64_t* mask, hipStream_t stream);
+
+/* Tree attention (EAGLE-2 page: each flattened token attends to the whole
+ * context and to its own ancestors only).  For sequence b, tree row i, query head
+ * h and KV head g = h / (n_q_heads / n_kv_heads):
+ *     keys  = cache rows kv_row_off[b] + c, c in [0, ctx_len[b])  (the context)
+ *             and kv_row_off[b] + ctx_len[b] + j for every j with mask bit j of row i
+ *     o     = softmax(scale * q . k) V ,   lse = log sum exp(scale * q . k)
+ * Layouts (dtype = storage type of q, k_cache, v_cache, o):
+ *     q, o      [batch][T][n_q_heads][head_dim]
+ *     k_cache,
+ *     v_cache   [n_kv_heads][kv_rows_total][head_dim]; sequence b owns rows
+ *               kv_row_off[b] .. kv_row_off[b] + ctx_len[b] + T - 1, its tree rows last,
+ *               in flattened order
+ *     mask      [batch][T] uint64 from eagle_tree_mask
+ *     lse       [batch][T][n_q_heads] fp32 natural log, or NULL
+ * BF16: fp32 accumulation, probabilities rounded to bf16 before the PV product,
+ * output rounded to nearest even.  F32: fp32 throughout.
+ * kv_rows_total must be at least sum_b (ctx_len[b] + T) (not checkable on the
+ * host; the call checks kv_rows_total >= batch * T).
+ * Supported: BF16 with head_dim 128 and batch <= 256; F32 with head_dim <= 128;
+ * T <= 64.
+ * The workspace (eagle_tree_attention_workspace bytes) must be zero-filled
+ * before its first use; every call leaves it zero-filled again. */
+typedef struct {
+    eagle_dtype dtype;
+    int32_t batch, T, n_q_heads, n_kv_heads, head_dim;
+    const int32_t* ctx_len;    /* [batch] device */
+    const int64_t* kv_row_off; /* [batch] device */
+    int64_t kv_rows_total;
+    float scale; /* 0 => 1/sqrt(head_dim) */
+} eagle_attn_desc;
+
+size_t eagle_tree_attention_workspace(const eagle_attn_desc* desc);
+
+int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void* k_cache,
+                         const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Verify (CSDN page 1.1/1.2, EAGLE page: the emitted tokens must follow the
+ * target's own distribution).  target_logits [batch][T][vocab] fp32: row i is the
+ * target's next-token logits after flattened row i.
+ *   temperature == 0: greedy -- starting at the root row, accept the child whose
+ *     token is the row's argmax (lowest id on ties) while one exists; the final
+ *     row's argmax is the bonus token.
+ *   temperature > 0: sampled -- p = softmax(z / temperature); the children of the
+ *     current row are tested in flattened order, child c accepted iff
+ *     u < p(tok c) / (mass of the tokens not yet rejected at this row); a rejected
+ *     child's token is removed.  With no acceptance (or no child) the bonus token
+ *     is the smallest t whose running residual mass exceeds u * (residual total).
+ *     u = top 24 bits / 2^24 of word 0 of Philox4x32-10 (Salmon et al., SC'11) with
+ *     key (seed low, seed high) and counter (slot, row, sequence, step low 32
+ *     bits); slot = child index, 0xFFFFFFFF for the bonus draw.
+ * Outputs: accept_len [batch] (0..depth), accept_path [batch][depth] (flattened
+ * rows, -1 padded), out_tokens [batch][depth + 1] (accepted tokens then the bonus,
+ * -1 padded).  flat_token / flat_parent from eagle_tree_mask.  Negative or NaN
+ * temperature is EAGLE_ERR_INVALID_ARG.  Workspace: eagle_verify_workspace bytes. */
+size_t eagle_verify_workspace(const eagle_tree_cfg* cfg);
+
+int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const int32_t* flat_token,
+                 const int32_t* flat_parent, float temperature, uint64_t seed, uint64_t step,
+                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code. */
+const char* eagle_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_TREE_H */

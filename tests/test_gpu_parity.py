@@ -1,0 +1,330 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: tree structure, values, kept sets, flattened arrays, masks, positions and
+greedy results bit-exact (tree rows whose fp64 log-normaliser the oracle flags
+as a rounding hazard are the only allowed difference); attention within 2e-2
+absolute for bf16 and 1e-5 for fp32; sampled acceptance identical except where
+the oracle records a decision within 1e-6 of its threshold.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ATOL_BF16 = 2e-2
+ATOL_F32 = 1e-5
+EXEMPT = 1e-6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_tree_verification_eagle_amd import binding, step, workload
+    return binding, step, workload
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def oracle_trees(orc, w, draft, root, ctx_lens):
+    out = []
+    for b in range(w.batch):
+        tree, kept, flat = orc.build_tree(draft[b], int(root[b]), w.depth, w.topk, w.m, w.n, int(ctx_lens[b]))
+        out.append((tree, kept, flat))
+    return out
+
+
+def mask_words(mask_tt):
+    T = mask_tt.shape[0]
+    words = np.zeros(T, dtype=np.uint64)
+    for i in range(T):
+        for j in np.nonzero(mask_tt[i])[0]:
+            words[i] |= np.uint64(1) << np.uint64(j)
+    return words
+
+
+def compare_trees(vs, trees):
+    """Bit-exact tree comparison; returns the number of sequences compared exactly."""
+    st = vs.state
+    tok = st.token.cpu().numpy(); par = st.parent.cpu().numpy(); dep = st.depth.cpu().numpy()
+    val = st.value.cpu().numpy(); nn = st.n_nodes.cpu().numpy()
+    kept = vs.kept.cpu().numpy()
+    ft = vs.flat_token.cpu().numpy(); fp = vs.flat_parent.cpu().numpy()
+    fd = vs.flat_depth.cpu().numpy(); pos = vs.position.cpu().numpy()
+    mk = vs.mask.cpu().numpy().view(np.uint64)
+    exact = 0
+    for b, (tree, okept, flat) in enumerate(trees):
+        n = tree["n_nodes"]
+        same = (nn[b] == n and np.array_equal(tok[b, :n], tree["token"]) and np.array_equal(par[b, :n], tree["parent"])
+                and np.array_equal(dep[b, :n], tree["depth"])
+                and np.array_equal(val[b, :n].view(np.uint32), tree["value"].view(np.uint32)))
+        if vs.w.n > 0:
+            same = same and np.array_equal(kept[b, :vs.w.n], okept)
+        same = same and np.array_equal(ft[b], flat["flat_token"]) and np.array_equal(fp[b], flat["flat_parent"])
+        same = same and np.array_equal(fd[b], flat["flat_depth"]) and np.array_equal(pos[b], flat["position"])
+        same = same and np.array_equal(mk[b], mask_words(flat["mask"]))
+        if not same:
+            assert tree["row_hazard"].any(), f"sequence {b}: GPU tree differs from the oracle with no rounding hazard"
+            say(f"sequence {b}: tree differs on a flagged fp64 rounding hazard (allowed)")
+        else:
+            exact += 1
+    return exact
+
+
+def to_f32(t):
+    return t.float().cpu().numpy()
+
+
+def attention_check(orc, vs, trees, layer, n_pairs_per_seq=None, seqs=None, atol=ATOL_BF16, seed=0):
+    """Compare GPU attention of one layer with the oracle on all or sampled (i, h)."""
+    w = vs.w
+    a = vs.attn[layer]
+    o_gpu = a["o"].float().cpu().numpy()
+    lse_gpu = a["lse"].cpu().numpy() if a["lse"] is not None else None
+    rng = np.random.default_rng(seed)
+    seqs = range(w.batch) if seqs is None else seqs
+    worst = 0.0
+    for b in seqs:
+        ctx = int(vs.ctx_lens_np[b]); r0 = int(vs.kv_off_np[b]); rows = ctx + w.T
+        k = to_f32(a["k"][:, r0:r0 + rows]); v = to_f32(a["v"][:, r0:r0 + rows])
+        q = to_f32(a["q"][b])
+        mask = trees[b][2]["mask"]
+        if n_pairs_per_seq is None:
+            o, lse = orc.attention(q, k, v, mask, ctx)
+            got = o_gpu[b]
+            err = np.abs(got - o).max()
+            lerr = np.abs(lse_gpu[b] - lse).max() if lse_gpu is not None else 0.0
+        else:
+            sel = [(int(i), int(h)) for i, h in zip(rng.integers(0, w.T, n_pairs_per_seq),
+                                                      rng.integers(0, w.n_q_heads, n_pairs_per_seq))]
+            sel += [(0, 0), (w.T - 1, w.n_q_heads - 1)]
+            o, lse = orc.attention(q, k, v, mask, ctx, sel=sel)
+            got = np.stack([o_gpu[b, i, h] for i, h in sel])
+            err = np.abs(got - o).max()
+            lerr = max(abs(lse_gpu[b, i, h] - lse[j]) for j, (i, h) in enumerate(sel)) if lse_gpu is not None else 0.0
+        assert np.isfinite(got).all()
+        assert err <= atol, f"seq {b} layer {layer}: max |o - oracle| = {err}"
+        assert lerr <= max(atol, 1e-4), f"seq {b} layer {layer}: max |lse - oracle| = {lerr}"
+        worst = max(worst, err)
+    return worst
+
+
+def planted_target(wl, w, trees):
+    ft = np.stack([t[2]["flat_token"] for t in trees])
+    fp = np.stack([t[2]["flat_parent"] for t in trees])
+    base = wl.target_logits_base(w)
+    return wl.plant(base, ft, fp, w.plant_frac, w.seed), ft, fp
+
+
+def verify_check(orc, vs, w, target, ft, fp, temperature, seed, steps):
+    """Run eagle_verify for several steps; compare with the oracle per sequence."""
+    vs.set_target(target)
+    exempt = 0
+    taus = []
+    for s in steps:
+        vs.verify(temperature, seed, s)
+        torch.cuda.synchronize()
+        al = vs.accept_len.cpu().numpy(); ap = vs.accept_path.cpu().numpy(); ot = vs.out_tokens.cpu().numpy()
+        for b in range(w.batch):
+            if temperature == 0.0:
+                l, p, o = orc.verify_greedy(target[b], ft[b], fp[b], w.depth)
+                tr = np.zeros((0, 4))
+            else:
+                l, p, o, tr = orc.verify_sampled(target[b], ft[b], fp[b], w.depth, temperature, seed, s, b)
+            same = al[b] == l and np.array_equal(ap[b], p) and np.array_equal(ot[b], o)
+            if not same:
+                assert temperature > 0.0, f"greedy mismatch seq {b} step {s}"
+                near = [row for row in tr if (row[1] >= 0 and abs(row[2] - row[3]) < EXEMPT) or
+                        (row[1] < 0 and row[3] < EXEMPT)]
+                assert near, f"sampled mismatch seq {b} step {s} with no decision within {EXEMPT}"
+                exempt += 1
+            taus.append(int(l) + 1)
+    return exempt, float(np.mean(taus))
+
+
+# ---------------------------------------------------------------------------
+# full workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_f32", "llama2_7b_layer", "llama2_13b", "llama2_70b_gqa", "batched_13b"])
+def test_tree_parity_full_workload(lib, orc, name):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS[name]
+    say(f"[tree parity] {name}")
+    vs = stepm.VerifyStep(w, layers=0)
+    vs.tree()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    exact = compare_trees(vs, trees)
+    assert exact >= w.batch - 1
+    # determinism: the same inputs again give the same bits
+    tok0 = vs.state.token.clone(); val0 = vs.state.value.clone(); m0 = vs.mask.clone()
+    vs.tree()
+    torch.cuda.synchronize()
+    assert torch.equal(tok0, vs.state.token) and torch.equal(val0, vs.state.value) and torch.equal(m0, vs.mask)
+
+
+def test_attention_parity_tiny_f32_all_outputs(lib, orc):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["tiny_f32"]
+    say("[attention parity] tiny_f32, every output")
+    vs = stepm.VerifyStep(w)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    attention_check(orc, vs, trees, 0, None, atol=ATOL_F32)
+
+
+def test_attention_parity_7b_layer_all_outputs(lib, orc):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["llama2_7b_layer"]
+    say("[attention parity] llama2_7b_layer, every output")
+    vs = stepm.VerifyStep(w)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    worst = attention_check(orc, vs, trees, 0, None)
+    say(f"  worst |o - oracle| = {worst:.2e}")
+
+
+def test_attention_parity_13b_sampled_layers(lib, orc):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["llama2_13b"]
+    say("[attention parity] llama2_13b, 2 layers at full size, sampled outputs")
+    vs = stepm.VerifyStep(w, layers=2)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    for layer in range(2):
+        attention_check(orc, vs, trees, layer, 120, seed=layer)
+        o = vs.attn[layer]["o"]
+        assert torch.isfinite(o.float()).all()
+    # repeated launches reuse the workspace: identical bits
+    o0 = vs.attn[0]["o"].clone()
+    vs.attention([0]); vs.attention([0])
+    torch.cuda.synchronize()
+    assert torch.equal(o0, vs.attn[0]["o"])
+
+
+def test_attention_parity_70b_gqa_sampled(lib, orc):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["llama2_70b_gqa"]
+    say("[attention parity] llama2_70b_gqa, 1 layer at full size, sampled outputs")
+    vs = stepm.VerifyStep(w, layers=1)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    attention_check(orc, vs, trees, 0, 160)
+
+
+def test_attention_parity_batched_ragged_sampled(lib, orc):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["batched_13b"]
+    say("[attention parity] batched_13b, 1 layer, 16 ragged sequences, sampled outputs")
+    vs = stepm.VerifyStep(w, layers=1)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    lens = vs.ctx_lens_np
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3, 11})
+    attention_check(orc, vs, trees, 0, 40, seqs=seqs)
+    assert torch.isfinite(vs.attn[0]["o"].float()).all()
+
+
+@pytest.mark.parametrize("name,temps", [("tiny_f32", (0.0,)), ("llama2_7b_layer", (0.0,)),
+                                        ("llama2_13b", (1.0,)), ("llama2_70b_gqa", (0.0, 0.7)),
+                                        ("batched_13b", (1.0,))])
+def test_verify_parity(lib, orc, name, temps):
+    eb, stepm, wl = lib
+    w = wl.CONFIGS[name]
+    vs = stepm.VerifyStep(w, layers=0)
+    vs.tree()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    target, ft, fp = planted_target(wl, w, trees)
+    for temp in temps:
+        steps = range(1) if temp == 0.0 else range(12)
+        say(f"[verify parity] {name} temperature {temp}")
+        exempt, tau = verify_check(orc, vs, w, target, ft, fp, temp, seed=2024 + w.seed, steps=steps)
+        say(f"  exempt decisions {exempt}, mean accepted+1 = {tau:.2f}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases on small shapes
+# ---------------------------------------------------------------------------
+def small(wl, **kw):
+    base = dict(name="edge", vocab=300, depth=3, topk=3, m=2, n=8, n_q_heads=4, n_kv_heads=4, head_dim=128,
+                layers=1, batch=1, ctx=70, ctx_range=None, dtype="bf16", draft_sigma=2.0, target_sigma=2.0,
+                temperatures=(0.0,), plant_frac=0.5, seed=77)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+EDGE = [
+    dict(n=0),                                             # root only, T = 1
+    dict(ctx=0),                                           # no context
+    dict(ctx=1, n=12), dict(ctx=63), dict(ctx=64), dict(ctx=65, n=15),
+    dict(batch=5, ctx_range=(0, 200), n=15, seed=5),       # ragged batch, stream-K across sequences
+    dict(n_q_heads=8, n_kv_heads=2, n=19, ctx=150, depth=4, m=3),  # GQA: 4 x 20 = 80 packed rows -> 2 row groups
+    dict(n_q_heads=6, n_kv_heads=1, n=15, ctx=33),         # GQA 6:1, 96 rows
+    dict(depth=1, topk=5, m=5, n=5, vocab=5),              # top-k = whole vocabulary
+    dict(depth=6, topk=1, m=1, n=6, ctx=10),               # chain tree
+    dict(depth=2, topk=32, m=32, n=63, vocab=2000, ctx=500),  # widest tree, T = 64
+    dict(dtype="f32", head_dim=64, ctx=37, n=10),
+    dict(dtype="f32", head_dim=128, n_q_heads=4, n_kv_heads=2, ctx=5, n=7),
+    dict(batch=3, ctx_range=(2000, 9000), n_q_heads=40, n_kv_heads=40, n=60, depth=6, topk=10, m=10,
+         vocab=4000, seed=9),                              # many units spread over many workgroups
+]
+
+
+@pytest.mark.parametrize("kw", EDGE, ids=[",".join(f"{k}={v}" for k, v in e.items()) for e in EDGE])
+def test_edge_cases(lib, orc, kw):
+    eb, stepm, wl = lib
+    w = small(wl, **kw)
+    say(f"[edge] {kw}")
+    vs = stepm.VerifyStep(w)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    compare_trees(vs, trees)
+    dense_work = w.T * w.n_q_heads * (int(vs.ctx_lens_np.max()) + w.T) * w.batch
+    attention_check(orc, vs, trees, 0, None if dense_work < 3e6 else 60,
+                    atol=ATOL_F32 if w.dtype == "f32" else ATOL_BF16)
+    target, ft, fp = planted_target(wl, w, trees)
+    verify_check(orc, vs, w, target, ft, fp, 0.0, 1, range(1))
+    verify_check(orc, vs, w, target, ft, fp, 0.9, 31, range(6))
+
+
+def test_branch_independence_on_gpu(lib, orc):
+    eb, stepm, wl = lib
+    w = small(wl, n=12, ctx=90)
+    vs = stepm.VerifyStep(w)
+    vs.tree(); vs.attention()
+    torch.cuda.synchronize()
+    mask = vs.mask.cpu().numpy().view(np.uint64)[0]
+    o0 = vs.attn[0]["o"].clone()
+    a = vs.attn[0]
+    ctx = int(vs.ctx_lens_np[0])
+    for j in (1, 5, w.T - 1):
+        k_keep = a["k"][:, ctx + j].clone()
+        v_keep = a["v"][:, ctx + j].clone()
+        a["k"][:, ctx + j] += 1.5
+        a["v"][:, ctx + j] -= 0.75
+        vs.attention()
+        torch.cuda.synchronize()
+        for i in range(w.T):
+            sees = bool((int(mask[i]) >> j) & 1)
+            same = torch.equal(a["o"][0, i], o0[0, i])
+            assert same != sees, f"row {i} vs perturbed tree row {j}"
+        a["k"][:, ctx + j] = k_keep
+        a["v"][:, ctx + j] = v_keep
