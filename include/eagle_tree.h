@@ -142,10 +142,11 @@ int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
  * output rounded to nearest even.  F32: fp32 throughout.
  * kv_rows_total must be at least sum_b (ctx_len[b] + T) (not checkable on the
  * host; the call checks kv_rows_total >= batch * T).
- * Supported: BF16 with head_dim 128 and batch <= 256; F32 with head_dim <= 128;
- * T <= 64.
- * The workspace (eagle_tree_attention_workspace bytes) must be zero-filled
- * before its first use; every call leaves it zero-filled again. */
+ * Supported: BF16 with head_dim 128; F32 with head_dim <= 128; T <= 64;
+ * batch <= EAGLE_MAX_BATCH.  BF16 runs one sequence per kernel launch pair.
+ * The workspace (eagle_tree_attention_workspace bytes, none for F32) holds
+ * split-KV partials; it needs no initialisation, and calls that share one must
+ * be ordered on one stream. */
 typedef struct {
     eagle_dtype dtype;
     int32_t batch, T, n_q_heads, n_kv_heads, head_dim;
