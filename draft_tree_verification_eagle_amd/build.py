@@ -23,6 +23,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
     # packed fp32 VALU forms stay off (plain VALU ops are generated instead)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the tree-attention softmax reads and
+    # rescales them every tile, which AGPR accumulators would turn into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

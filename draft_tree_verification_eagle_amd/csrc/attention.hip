@@ -28,7 +28,11 @@
 //    from the row-major V tile through ds_read_b64_tr_b16.  The key order inside
 //    the S^T block is permuted so each half-wave's probabilities are the PV
 //    operand's 8 consecutive keys, with no register shuffles.  Online softmax in
-//    fp32 (base 2); probabilities rounded to bf16 for PV.
+//    fp32 (base 2) with a lazy reference max: O is rescaled only when a row's max
+//    grows by more than 2^8, so the common tile does no rescale; probabilities
+//    are rounded to bf16 for PV.  The MFMA accumulators live in VGPRs (the library
+//    is built with the VGPR form of MFMA), so the softmax and rescale read them
+//    without accumulator-register copies.
 //  * A workgroup whose stretch holds a whole unit writes the output; otherwise
 //    it writes a partial: row max and row sum in fp32 and the normalised row in
 //    fp16 (relative rounding 2^-11, inside the bf16 output's own).  The merge
@@ -65,6 +69,7 @@ constexpr int kQBytes = kUnitRows * kRowBytes;       // 16 KB
 constexpr int kKVLoads = 2 * kTileBytes / (kThreads * 16);  // 8 per thread per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised probability
 
 static_assert(kKVLoads == 8 && kStages == 4, "the stage barriers assume 8 loads per tile, 4 stages");
 
@@ -84,10 +89,20 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // Nothing else in this kernel uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_b128(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16 bytes per lane from base + off (scalar base, 32-bit lane offset) to LDS
+// address lds + 16 * lane.
+// The base is the same in every lane; readfirstlane makes that visible to the
+// compiler so the operand is always an SGPR pair.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t off, uint32_t lds_addr) {
+    // readfirstlane returns int: widen through uint32_t (a sign extension of the
+    // low word would corrupt the high word of the address)
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"((const void*)(uintptr_t)bu)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds_addr) {
@@ -102,6 +117,10 @@ __device__ __forceinline__ void barrier_vm8() { asm volatile("s_waitcnt vmcnt(8)
 __device__ __forceinline__ void barrier_vm0() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Barrier for LDS traffic only (leaves the K/V loads in flight).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Stage barrier given the number of tiles fetched after the awaited one.
+__device__ __forceinline__ void barrier_after(int after) {
+    if (after >= 2) barrier_vm16(); else if (after == 1) barrier_vm8(); else barrier_vm0();
+}
 
 // s_waitcnt vmcnt(0) as the compiler sees it: after this, registers filled by
 // ordinary loads count as complete, so no wait for them is carried into the
@@ -110,6 +129,16 @@ __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// max / sum of a value over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // One sequence.  Pointers are already offset to the sequence.
@@ -123,7 +152,7 @@ struct AttnArgs {
     const int32_t* ctx_len;    // [1]
     const int64_t* kv_row_off; // [1]
     _Float16* part_o;          // [slots][64][128], normalised rows
-    float* part_ml;            // [slots][2][64]: row max (base 2), row sum
+    float* part_ml;            // [slots][2][64]: row reference max (base 2), row sum
     int64_t kv_rows_total;
     int T, Hq, Hkv, G, RG;
     float scale_log2;
@@ -137,22 +166,35 @@ __device__ __forceinline__ int stretch_of(int64_t x, int64_t total, int nwg) {
     return v;
 }
 
-// Tile at list position x: unit, first key, key count, segment flags.
+// Position in a workgroup's stretch of the unit-major key list: list position x,
+// unit and key inside the unit.  Advanced tile by tile without division.
+struct Walker {
+    int64_t x;
+    int unit, key0;
+};
 struct Tile {
     int unit, key0, nkeys;
     bool seg_start, seg_end;
 };
-__device__ __forceinline__ Tile tile_at(int64_t x, int64_t x_begin, int64_t x_end, int S) {
+__device__ __forceinline__ Tile peek(const Walker& w, int64_t x_begin, int64_t x_end, int S) {
     Tile t;
-    t.unit = uni((int)(x / S));
-    t.key0 = uni((int)(x - (int64_t)t.unit * S));
+    t.unit = w.unit;
+    t.key0 = w.key0;
     int n = kTileKeys;
-    if (S - t.key0 < n) n = S - t.key0;
-    if (x_end - x < n) n = (int)(x_end - x);
-    t.nkeys = uni(n);
-    t.seg_start = (x == x_begin) || (t.key0 == 0);
-    t.seg_end = (x + t.nkeys == x_end) || (t.key0 + t.nkeys == S);
+    if (S - w.key0 < n) n = S - w.key0;
+    if (x_end - w.x < n) n = (int)(x_end - w.x);
+    t.nkeys = n;
+    t.seg_start = (w.x == x_begin) || (w.key0 == 0);
+    t.seg_end = (w.x + n == x_end) || (w.key0 + n == S);
     return t;
+}
+__device__ __forceinline__ void advance(Walker& w, int nkeys, int S) {
+    w.x += nkeys;
+    w.key0 += nkeys;
+    if (w.key0 == S) {
+        w.key0 = 0;
+        ++w.unit;
+    }
 }
 
 // Packed query row -> (tree row, query head); rows past G*T map to row 0.
@@ -163,20 +205,32 @@ __device__ __forceinline__ void query_row(const AttnArgs& a, int g, int rp, int&
     hq = g * a.G + gi;
 }
 
-// Direct-to-LDS loads of one tile's K and V rows: always 8 per thread; rows
-// past nkeys re-read row nkeys - 1.
+// Direct-to-LDS loads of one tile's K and V rows: always 8 per thread.  Lane
+// offsets for a full tile are precomputed; for a short tile, rows past nkeys
+// re-read row nkeys - 1 (masked out by the softmax, no extra HBM traffic).
 __device__ __forceinline__ void issue_kv(const AttnArgs& a, const Tile& t, int64_t row0, unsigned char* st,
-                                         int wid, int lane) {
+                                         const uint32_t (&off_full)[4], int wid, int lane) {
     const int g = t.unit / a.RG;
-    const int64_t base = ((int64_t)g * a.kv_rows_total + row0 + t.key0) * kD;
+    const int64_t elt0 = ((int64_t)g * a.kv_rows_total + row0 + t.key0) * kD;
+    const __bf16* kb = a.k + elt0;
+    const __bf16* vb = a.v + elt0;
+    if (t.nkeys == kTileKeys) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int blk = n * 4 + wid;  // 16 blocks of 4 rows
-        const int lrow = blk * 4 + (lane >> 4);
-        const int grow = lrow < t.nkeys ? lrow : t.nkeys - 1;
-        const int c = (lane & 15) ^ swz(lrow);
-        dma_b128(a.k + base + (int64_t)grow * kD + c * 8, lds_u32(st + blk * 1024));
-        dma_b128(a.v + base + (int64_t)grow * kD + c * 8, lds_u32(st + kTileBytes + blk * 1024));
+        for (int n = 0; n < 4; ++n) {
+            const int blk = n * 4 + wid;  // 16 blocks of 4 rows
+            dma_b128(kb, off_full[n], lds_u32(st + blk * 1024));
+            dma_b128(vb, off_full[n], lds_u32(st + kTileBytes + blk * 1024));
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int blk = n * 4 + wid;
+            const int lrow = blk * 4 + (lane >> 4);
+            const int grow = lrow < t.nkeys ? lrow : t.nkeys - 1;
+            const uint32_t off = (uint32_t)(grow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
+            dma_b128(kb, off, lds_u32(st + blk * 1024));
+            dma_b128(vb, off, lds_u32(st + kTileBytes + blk * 1024));
+        }
     }
 }
 
@@ -190,8 +244,8 @@ __device__ __forceinline__ void issue_q(const AttnArgs& a, int unit, unsigned ch
         const int rho = blk * 4 + (lane >> 4);
         int i, hq;
         query_row(a, g, rg * kUnitRows + rho, i, hq);
-        const int c = (lane & 15) ^ swz(rho);
-        dma_b128(a.q + ((int64_t)i * a.Hq + hq) * kD + c * 8, lds_u32(qslot + blk * 1024));
+        const uint32_t off = (uint32_t)((((int64_t)i * a.Hq + hq) * kD) * 2 + (((lane & 15) ^ swz(rho)) << 4));
+        dma_b128(a.q, off, lds_u32(qslot + blk * 1024));
     }
     if (wid == 0) {
         int i, hq;
@@ -222,39 +276,77 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     if (vwg >= nwg) return;
     const int64_t x_begin = total * vwg / nwg, x_end = total * (vwg + 1) / nwg;
 
+    uint32_t off_full[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int lrow = (n * 4 + wid) * 4 + (lane >> 4);
+        off_full[n] = (uint32_t)(lrow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
+    }
+
+    Walker w0;
+    w0.x = x_begin;
+    w0.unit = (int)(x_begin / S);
+    w0.key0 = (int)(x_begin - (int64_t)w0.unit * S);
+
     // ---- first segment's Q and mask word, straight into registers ----
     const int qrow = 32 * rb + l32;  // this lane's packed query row inside the unit
     bf16x8 qcur[8];
-    uint64_t mword;
-    {
-        const Tile t0 = tile_at(x_begin, x_begin, x_end, S);
-        const int g = t0.unit / a.RG, rg = t0.unit - g * a.RG;
+    uint64_t mword_n;
+    auto load_q_direct = [&](int unit) {
+        const int g = unit / a.RG, rg = unit - g * a.RG;
         int i, hq;
         query_row(a, g, rg * kUnitRows + qrow, i, hq);
         const __bf16* qp = a.q + ((int64_t)i * a.Hq + hq) * kD;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qcur[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * h2);
-        mword = a.mask[i];
+        mword_n = a.mask[i];
         wait_direct_loads();
-    }
+    };
+    load_q_direct(w0.unit);
 
     // ---- prologue: tiles 0..2 in flight; a later segment's Q goes to the slot ----
-    int64_t xl = x_begin;     // list position of the next tile to fetch
+    Walker wf = w0;           // next tile to fetch
     int nl = 0;               // tiles fetched so far
     int q_slot_tile = -1;     // tile whose Q is in (or on its way to) the Q slot
     // A later segment's Q rides with its first tile into the slot when the slot is
-    // free; otherwise that tile loads its Q directly when it is computed.
+    // free; otherwise that tile loads its Q directly when its scores are computed.
     auto fetch = [&]() {
-        const Tile t = tile_at(xl, x_begin, x_end, S);
-        issue_kv(a, t, row0, smem + (nl % kStages) * kStageBytes, wid, lane);
+        const Tile t = peek(wf, x_begin, x_end, S);
+        issue_kv(a, t, row0, smem + (nl % kStages) * kStageBytes, off_full, wid, lane);
         if (t.seg_start && nl > 0 && q_slot_tile < 0) {
             issue_q(a, t.unit, qslot, mslot, wid, lane);
             q_slot_tile = nl;
         }
-        xl += t.nkeys;
+        advance(wf, t.nkeys, S);
         ++nl;
     };
-    for (int s = 0; s < kStages - 1 && xl < x_end; ++s) fetch();
+    for (int s = 0; s < kStages - 1 && wf.x < x_end; ++s) fetch();
+
+    const int krow = 32 * ks + key_of_row(l32);
+    const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
+
+    // S^T = K Q^T for this wave's 32 keys x 32 query rows of the tile in stage st
+    auto scores = [&](const unsigned char* st) {
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int c = (2 * kk + h2) ^ swz(krow);
+            const bf16x8 kv = *(const bf16x8*)(st + krow * kRowBytes + c * 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qcur[kk], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+
+    // ---- tile 0: wait, scores ----
+    barrier_after(nl - 1);
+    Walker wn = w0;           // tile whose scores are computed next
+    Tile tc = peek(wn, x_begin, x_end, S);
+    advance(wn, tc.nkeys, S);
+    f32x16 sacc = scores(smem);
+    uint64_t mword_c = mword_n;
+    bool from0_c = tc.key0 == 0;  // the current segment starts at the unit's first key
 
     f32x16 oacc[4];
 #pragma unroll
@@ -262,102 +354,79 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
-    int seg_key0 = 0;
-    const int krow = 32 * ks + key_of_row(l32);
-    const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
 
-    int64_t xc = x_begin;     // list position of the tile being computed
-    for (int it = 0; xc < x_end; ++it) {
-        // tiles fetched after this one: nl - 1 - it (at most 2)
-        const int after = nl - 1 - it;
-        if (after >= 2) barrier_vm16(); else if (after == 1) barrier_vm8(); else barrier_vm0();
-        if (xl < x_end) fetch();
-
-        const Tile tc = tile_at(xc, x_begin, x_end, S);
-        unsigned char* st = smem + (it % kStages) * kStageBytes;
-        const unsigned char* sK = st;
-        const unsigned char* sV = st + kTileBytes;
-
-        if (tc.seg_start) {
-            if (it > 0) {
-                if (q_slot_tile == it) {
+    // Software pipeline: iteration it computes the scores of tile it+1 (MFMA)
+    // next to the softmax of tile it (VALU), then PV of tile it.
+    for (int it = 0;; ++it) {
+        const bool has_next = wn.x < x_end;
+        Tile tn;
+        f32x16 snext;
+        bool from0_n = from0_c;
+        if (has_next) {
+            barrier_after(nl - it - 2);  // tile it+1 has landed; tile it-1's stage is free
+            if (wf.x < x_end) fetch();
+            tn = peek(wn, x_begin, x_end, S);
+            if (tn.seg_start) {
+                if (q_slot_tile == it + 1) {
 #pragma unroll
                     for (int kk = 0; kk < 8; ++kk) {
                         const int c = (2 * kk + h2) ^ swz(qrow);
                         qcur[kk] = *(const bf16x8*)(qslot + qrow * kRowBytes + c * 16);
                     }
-                    mword = (uint64_t)mslot[qrow] | ((uint64_t)mslot[kWave + qrow] << 32);
+                    mword_n = (uint64_t)mslot[qrow] | ((uint64_t)mslot[kWave + qrow] << 32);
                     q_slot_tile = -1;  // free once every wave has passed the next barrier
                 } else {
-                    const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
-                    int i, hq;
-                    query_row(a, g, rg * kUnitRows + qrow, i, hq);
-                    const __bf16* qp = a.q + ((int64_t)i * a.Hq + hq) * kD;
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) qcur[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * h2);
-                    mword = a.mask[i];
-                    wait_direct_loads();  // drains the K/V loads too: rare (short segments)
+                    load_q_direct(tn.unit);  // drains the K/V loads too: rare (short segments)
                 }
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-                m_run = -INFINITY;
-                l_run = 0.0f;
+                from0_n = tn.key0 == 0;
             }
-            seg_key0 = tc.key0;
+            snext = scores(smem + ((it + 1) % kStages) * kStageBytes);
         }
 
-        // ---- S^T = K Q^T: this wave's 32 keys x 32 query rows, two MFMA chains ----
-        f32x16 s0, s1;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { s0[e] = 0.0f; s1[e] = 0.0f; }
-#pragma unroll
-        for (int kk = 0; kk < 8; kk += 2) {
-            const int c0 = (2 * kk + h2) ^ swz(krow), c1 = (2 * kk + 2 + h2) ^ swz(krow);
-            const bf16x8 k0 = *(const bf16x8*)(sK + krow * kRowBytes + c0 * 16);
-            const bf16x8 k1 = *(const bf16x8*)(sK + krow * kRowBytes + c1 * 16);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qcur[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qcur[kk + 1], s1, 0, 0, 0);
-        }
+        const unsigned char* st = smem + (it % kStages) * kStageBytes;
+        const unsigned char* sV = st + kTileBytes;
 
         // ---- online softmax (base 2): lane = one query row, 16 of its keys ----
-        float sv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sv[e] = (s0[e] + s1[e]) * a.scale_log2;
+        // Raw scores; the scale (> 0) is applied inside the exponent.
         if (tc.key0 + kTileKeys > ctx || tc.nkeys < kTileKeys) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int j = 32 * ks + 16 * (e >> 3) + 8 * h2 + (e & 7);
                 const int key = tc.key0 + j;
                 bool vis = j < tc.nkeys;
-                if (vis && key >= ctx) vis = (mword >> (key - ctx)) & 1ull;
-                if (!vis) sv[e] = -INFINITY;
+                if (vis && key >= ctx) vis = (mword_c >> (key - ctx)) & 1ull;
+                if (!vis) sacc[e] = -INFINITY;
             }
         }
-        float mx = sv[0];
+        float mx = fmaxf(sacc[0], sacc[1]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        float psum = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float p = exp2f(sv[e] - m_use);
-            psum += p;
-            pb[e >> 3][e & 7] = (__bf16)p;
-        }
-        l_run = l_run * alpha + psum;
-        if (__any(alpha != 1.0f && m_run != -INFINITY)) {
+        for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+        mx = pair_max(mx) * a.scale_log2;
+        // Lazy rescaling: the running reference max moves only when a row's max
+        // exceeds it by more than kLazy (so probabilities stay <= 2^kLazy).  Any
+        // reference gives the same softmax; this keeps the O rescale off the
+        // common path.
+        if (__any(mx > m_run + kLazy)) {
+            const bool bump = mx > m_run + kLazy;
+            // exp2(-inf) = 0 when the row had no visible key yet (O and l are 0)
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            if (bump) m_run = mx;
         }
-        m_run = m_new;
+        const float nm = (m_run == -INFINITY) ? 0.0f : -m_run;
+        float psum = 0.0f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, nm));
+            psum += p;
+            pb[e >> 3][e & 7] = (__bf16)p;
+        }
+        l_run += psum;
 
         // ---- O^T += V^T P^T; V^T operands by LDS transpose reads ----
 #pragma unroll
@@ -394,14 +463,13 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             barrier_lds();
             if (ks == 0) {
                 const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
-                const bool whole = seg_key0 == 0 && tc.key0 + tc.nkeys == S;
+                const bool whole = from0_c && tc.key0 + tc.nkeys == S;
                 const int rp = rg * kUnitRows + qrow;
                 const float m1 = s_ml[rb][0][lane], l1 = s_ml[rb][1][lane];
                 const float M = fmaxf(m_run, m1);
                 const float Mu = (M == -INFINITY) ? 0.0f : M;
-                const float a0 = exp2f(m_run - Mu), a1 = exp2f(m1 - Mu);
-                const float lsum = l_run * a0 + l1 * a1;
-                const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+                const float a0 = __builtin_amdgcn_exp2f(m_run - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+                const float ltot = pair_sum(l_run * a0 + l1 * a1);
                 // a row that sees none of this segment's keys has ltot = 0: its partial
                 // is all zeros, and its merge weight is zero
                 const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
@@ -444,13 +512,26 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                     }
                 }
             }
+            // the next segment starts from an empty state
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+            m_run = -INFINITY;
+            l_run = 0.0f;
         }
-        xc += tc.nkeys;
+        if (!has_next) break;
+        sacc = snext;
+        tc = tn;
+        advance(wn, tn.nkeys, S);
+        mword_c = mword_n;
+        from0_c = from0_n;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Merge: one workgroup per (unit, 16 query rows); thread = (row, 8 dims).
+// Partials are combined four at a time, their loads issued together.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg) {
     const int tid = threadIdx.x;
@@ -466,31 +547,48 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
     const int d0 = (tid & 15) * 8;
     const int rp = rg * kUnitRows + row;
     if (rp >= a.G * a.T) return;
-    float M = -INFINITY;
-    for (int v = vf; v <= vl; ++v) M = fmaxf(M, a.part_ml[((int64_t)unit + v) * 128 + row]);
-    float L = 0.0f;
-    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int v = vf; v <= vl; ++v) {
-        const int64_t slot = (int64_t)unit + v;
-        const float w = exp2f(a.part_ml[slot * 128 + row] - M) * a.part_ml[slot * 128 + 64 + row];
-        L += w;
-        const f16x8 o8 = *(const f16x8*)(a.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
+    float M = -INFINITY, L = 0.0f;
+    float acc[8];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            acc0[x] += (float)o8[x] * w;
-            acc1[x] += (float)o8[4 + x] * w;
+    for (int x = 0; x < 8; ++x) acc[x] = 0.0f;
+    for (int v0 = vf; v0 <= vl; v0 += 4) {
+        float mv[4], lv[4];
+        f16x8 ov[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t slot = (int64_t)unit + v0 + j;
+            if (v0 + j <= vl) {
+                mv[j] = a.part_ml[slot * 128 + row];
+                lv[j] = a.part_ml[slot * 128 + 64 + row];
+                ov[j] = *(const f16x8*)(a.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
+            } else {
+                mv[j] = -INFINITY;
+                lv[j] = 0.0f;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) ov[j][x] = (_Float16)0.0f;
+            }
         }
+        const float Mn = fmaxf(fmaxf(M, fmaxf(mv[0], mv[1])), fmaxf(mv[2], mv[3]));
+        const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+        const float sc = __builtin_amdgcn_exp2f(M - Mu);
+        L *= sc;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] *= sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = __builtin_amdgcn_exp2f(mv[j] - Mu) * lv[j];
+            L += w;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[x] += (float)ov[j][x] * w;
+        }
+        M = Mn;
     }
     int i, hq;
     query_row(a, g, rp, i, hq);
     const float inv = 1.0f / L;
     bf16x8 out;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        out[x] = (__bf16)(acc0[x] * inv);
-        out[4 + x] = (__bf16)(acc1[x] * inv);
-    }
+    for (int x = 0; x < 8; ++x) out[x] = (__bf16)(acc[x] * inv);
     *(bf16x8*)(a.o + ((int64_t)i * a.Hq + hq) * kD + d0) = out;
     if (d0 == 0 && a.lse) a.lse[(int64_t)i * a.Hq + hq] = (M + log2f(L)) * kLn2;
 }
