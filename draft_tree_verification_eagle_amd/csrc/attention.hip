@@ -105,6 +105,17 @@ __device__ __forceinline__ void dma_b128(const void* base, uint32_t off, uint32_
                  : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"((const void*)(uintptr_t)bu)
                  : "memory", "m0");
 }
+// Same, non-temporal: K and V are streamed once.
+__device__ __forceinline__ void dma_b128_nt(const void* base, uint32_t off, uint32_t lds_addr) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"((const void*)(uintptr_t)bu)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :
@@ -113,6 +124,7 @@ __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds_addr) {
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void barrier_vm16() { asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void barrier_vm24() { asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void barrier_vm8() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void barrier_vm0() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Barrier for LDS traffic only (leaves the K/V loads in flight).
@@ -218,8 +230,8 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, const Tile& t, int64
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int blk = n * 4 + wid;  // 16 blocks of 4 rows
-            dma_b128(kb, off_full[n], lds_u32(st + blk * 1024));
-            dma_b128(vb, off_full[n], lds_u32(st + kTileBytes + blk * 1024));
+            dma_b128_nt(kb, off_full[n], lds_u32(st + blk * 1024));
+            dma_b128_nt(vb, off_full[n], lds_u32(st + kTileBytes + blk * 1024));
         }
     } else {
 #pragma unroll
@@ -228,8 +240,8 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, const Tile& t, int64
             const int lrow = blk * 4 + (lane >> 4);
             const int grow = lrow < t.nkeys ? lrow : t.nkeys - 1;
             const uint32_t off = (uint32_t)(grow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
-            dma_b128(kb, off, lds_u32(st + blk * 1024));
-            dma_b128(vb, off, lds_u32(st + kTileBytes + blk * 1024));
+            dma_b128_nt(kb, off, lds_u32(st + blk * 1024));
+            dma_b128_nt(vb, off, lds_u32(st + kTileBytes + blk * 1024));
         }
     }
 }
@@ -302,12 +314,14 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         mword_n = a.mask[i];
         wait_direct_loads();
     };
-    load_q_direct(w0.unit);
 
     // ---- prologue: tiles 0..2 in flight; a later segment's Q goes to the slot ----
     Walker wf = w0;           // next tile to fetch
     int nl = 0;               // tiles fetched so far
-    int q_slot_tile = -1;     // tile whose Q is in (or on its way to) the Q slot
+    int q_slot_tile = 0;      // tile whose Q is in (or on its way to) the Q slot
+    // The first segment's Q goes through the slot too, issued ahead of the first
+    // tiles so that its latency overlaps their streaming.
+    issue_q(a, w0.unit, qslot, mslot, wid, lane);
     // A later segment's Q rides with its first tile into the slot when the slot is
     // free; otherwise that tile loads its Q directly when its scores are computed.
     auto fetch = [&]() {
@@ -321,6 +335,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         ++nl;
     };
     for (int s = 0; s < kStages - 1 && wf.x < x_end; ++s) fetch();
+    // The Q loads were issued before the nl tiles' 8 * nl loads: wait for them only.
+    if (nl >= 3) barrier_vm24(); else if (nl == 2) barrier_vm16(); else barrier_vm8();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const int c = (2 * kk + h2) ^ swz(qrow);
+        qcur[kk] = *(const bf16x8*)(qslot + qrow * kRowBytes + c * 16);
+    }
+    mword_n = (uint64_t)mslot[qrow] | ((uint64_t)mslot[kWave + qrow] << 32);
+    q_slot_tile = -1;  // free once every wave has passed the tile-0 barrier
 
     const int krow = 32 * ks + key_of_row(l32);
     const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
@@ -360,7 +383,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     for (int it = 0;; ++it) {
         const bool has_next = wn.x < x_end;
         Tile tn;
-        f32x16 snext;
         bool from0_n = from0_c;
         if (has_next) {
             barrier_after(nl - it - 2);  // tile it+1 has landed; tile it-1's stage is free
@@ -380,7 +402,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 }
                 from0_n = tn.key0 == 0;
             }
-            snext = scores(smem + ((it + 1) % kStages) * kStageBytes);
         }
 
         const unsigned char* st = smem + (it % kStages) * kStageBytes;
@@ -418,17 +439,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             if (bump) m_run = mx;
         }
         const float nm = (m_run == -INFINITY) ? 0.0f : -m_run;
-        float psum = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, nm));
-            psum += p;
-            pb[e >> 3][e & 7] = (__bf16)p;
-        }
-        l_run += psum;
 
-        // ---- O^T += V^T P^T; V^T operands by LDS transpose reads ----
+        // ---- one branch-free block: the scores of tile it+1 on the matrix cores
+        // interleaved with this tile's exponentials on the VALU.  After the last
+        // tile the scores are computed from a stale stage and discarded. ----
+        // V^T operands of this tile's PV, read first so their latency overlaps
+        bf16x8 vop[2][4];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int vr1 = 32 * ks + 16 * j + 8 * h2 + rr;
@@ -442,23 +458,60 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_ADDR(i16x4, p1));
                 const i16x4 a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_ADDR(i16x4, p2));
                 const i16x8 a8 = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[j],
-                                                                   oacc[db], 0, 0, 0);
+                vop[j][db] = __builtin_bit_cast(bf16x8, a8);
             }
         }
+        const unsigned char* sKn = smem + ((it + 1) % kStages) * kStageBytes;
+        f32x16 snext;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) snext[e] = 0.0f;
+        float psum = 0.0f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int c = (2 * kk + h2) ^ swz(krow);
+            const bf16x8 kv = *(const bf16x8*)(sKn + krow * kRowBytes + c * 16);
+            snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qcur[kk], snext, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = 2 * kk + u;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.scale_log2, nm));
+                psum += p;
+                pb[e >> 3][e & 7] = (__bf16)p;
+            }
+        }
+        l_run += psum;
+
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j][db], pb[j], oacc[db], 0, 0, 0);
 
         if (tc.seg_end) {
-            // ---- merge the two key halves through this stage's LDS (its tile is
-            // consumed; the stage is refilled only after the next stage barrier) ----
-            barrier_lds();
-            float* mb = (float*)st;
+            // ---- merge the two key halves: the second half leaves its rows,
+            // normalised by its own row sum, in fp16 (relative rounding 2^-11) in
+            // this stage's K area, which the scores consumed an iteration ago and
+            // which is refilled only after the next stage barrier ----
+            // Without a next tile no stage barrier has passed since the scores of
+            // this tile were read from K: wait for every wave before overwriting it.
+            if (!has_next) barrier_lds();
+            const float lw = pair_sum(l_run);  // this wave's row sum over its keys
+            f16x4* mo = (f16x4*)st;            // [2 rb][4 db][4 q][64 lanes], 16 KB
             if (ks == 1) {
+                const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) mb[((rb * 64) + db * 16 + e) * kWave + lane] = oacc[db][e];
+                    for (int qd = 0; qd < 4; ++qd) {
+                        f16x4 w;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) w[x] = (_Float16)(oacc[db][4 * qd + x] * inv);
+                        mo[((rb * 4 + db) * 4 + qd) * kWave + lane] = w;
+                    }
                 s_ml[rb][0][lane] = m_run;
-                s_ml[rb][1][lane] = l_run;
+                s_ml[rb][1][lane] = lw;
             }
             barrier_lds();
             if (ks == 0) {
@@ -468,16 +521,21 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 const float m1 = s_ml[rb][0][lane], l1 = s_ml[rb][1][lane];
                 const float M = fmaxf(m_run, m1);
                 const float Mu = (M == -INFINITY) ? 0.0f : M;
-                const float a0 = __builtin_amdgcn_exp2f(m_run - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
-                const float ltot = pair_sum(l_run * a0 + l1 * a1);
+                const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
+                const float w1 = __builtin_amdgcn_exp2f(m1 - Mu) * l1;
+                const float ltot = lw * a0 + w1;
                 // a row that sees none of this segment's keys has ltot = 0: its partial
                 // is all zeros, and its merge weight is zero
                 const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        oacc[db][e] = (oacc[db][e] * a0 + mb[((rb * 64) + db * 16 + e) * kWave + lane] * a1) * inv;
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const f16x4 o1 = mo[((rb * 4 + db) * 4 + qd) * kWave + lane];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            oacc[db][4 * qd + x] = (oacc[db][4 * qd + x] * a0 + (float)o1[x] * w1) * inv;
+                    }
                 if (rp < a.G * T) {
                     if (whole) {
                         int i, hq;
