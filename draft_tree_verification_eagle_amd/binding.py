@@ -46,7 +46,8 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
     P, i32, u64, sz = C.c_void_p, C.c_int32, C.c_uint64, C.c_size_t
     L.eagle_tree_capacity.argtypes = [P]; L.eagle_tree_capacity.restype = i32
     L.eagle_tree_frontier_rows.argtypes = [P, i32]; L.eagle_tree_frontier_rows.restype = i32
-    L.eagle_tree_expand.argtypes = [P, i32, P, P, P, P]; L.eagle_tree_expand.restype = C.c_int
+    L.eagle_tree_expand_workspace.argtypes = [P]; L.eagle_tree_expand_workspace.restype = sz
+    L.eagle_tree_expand.argtypes = [P, i32, P, P, P, P, sz, P]; L.eagle_tree_expand.restype = C.c_int
     L.eagle_tree_rerank.argtypes = [P, P, P, P]; L.eagle_tree_rerank.restype = C.c_int
     L.eagle_tree_mask.argtypes = [P, P, P, P, P, P, P, P, P, P]; L.eagle_tree_mask.restype = C.c_int
     L.eagle_tree_attention_workspace.argtypes = [P]; L.eagle_tree_attention_workspace.restype = sz
@@ -133,10 +134,17 @@ def eagle_tree_frontier_rows(cfg: TreeCfg, layer: int) -> int:
     return _lib.eagle_tree_frontier_rows(C.byref(cfg), layer)
 
 
-def eagle_tree_expand(cfg: TreeCfg, layer: int, draft_logits, root_token, state: TreeState, stream=None):
+def eagle_tree_expand_workspace(cfg: TreeCfg) -> int:
+    return _lib.eagle_tree_expand_workspace(C.byref(cfg))
+
+
+def eagle_tree_expand(cfg: TreeCfg, layer: int, draft_logits, root_token, state: TreeState, workspace,
+                      stream=None):
     st = state.c_struct()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("eagle_tree_expand", _lib.eagle_tree_expand(C.byref(cfg), layer, _ptr(draft_logits),
-                                                       _ptr(root_token), C.byref(st), _stream(stream)))
+                                                       _ptr(root_token), C.byref(st), _ptr(workspace),
+                                                       nbytes, _stream(stream)))
 
 
 def eagle_tree_rerank(cfg: TreeCfg, state: TreeState, kept, stream=None):

@@ -28,6 +28,7 @@ bool tree_shape(const eagle_tree_cfg* c, int32_t* capacity) {
 int tree_limits(const eagle_tree_cfg* c, int32_t* cap) {
     if (!tree_cfg_ok(c)) return EAGLE_ERR_INVALID_ARG;
     if (c->topk > EAGLE_MAX_TOPK || c->depth > 255 || (int64_t)c->m * c->topk > EAGLE_MAX_LAYER_NODES ||
+        c->vocab > EAGLE_MAX_VOCAB ||
         c->n + 1 > EAGLE_MAX_TREE_ROWS || !tree_shape(c, cap))
         return EAGLE_ERR_UNSUPPORTED;
     if (c->n > *cap - 1) return EAGLE_ERR_INVALID_ARG;
@@ -57,8 +58,15 @@ int32_t eagle_tree_frontier_rows(const eagle_tree_cfg* cfg, int32_t layer) {
     return (int32_t)f;
 }
 
+size_t eagle_tree_expand_workspace(const eagle_tree_cfg* cfg) {
+    int32_t cap = 0;
+    if (tree_limits(cfg, &cap) != EAGLE_OK) return 0;
+    return eagle::expand_workspace_bytes(*cfg);
+}
+
 int eagle_tree_expand(const eagle_tree_cfg* cfg, int32_t layer, const float* draft_logits,
-                      const int32_t* root_token, const eagle_tree_state* state, hipStream_t stream) {
+                      const int32_t* root_token, const eagle_tree_state* state, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     int32_t cap = 0;
     const int st = tree_limits(cfg, &cap);
     if (st != EAGLE_OK) return st;
@@ -66,8 +74,10 @@ int eagle_tree_expand(const eagle_tree_cfg* cfg, int32_t layer, const float* dra
         return EAGLE_ERR_INVALID_ARG;
     if (cfg->batch == 0) return EAGLE_OK;
     if (!draft_logits) return EAGLE_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < eagle::expand_workspace_bytes(*cfg)) return EAGLE_ERR_WORKSPACE;
     const int rows = eagle_tree_frontier_rows(cfg, layer);
-    return from_hip(eagle::launch_expand(*cfg, layer, rows, cap, draft_logits, root_token, *state, stream));
+    return from_hip(eagle::launch_expand(*cfg, layer, rows, cap, draft_logits, root_token, *state,
+                                         workspace, stream));
 }
 
 int eagle_tree_rerank(const eagle_tree_cfg* cfg, const eagle_tree_state* state, int32_t* kept,

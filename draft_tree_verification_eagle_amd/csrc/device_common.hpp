@@ -24,39 +24,92 @@ __device__ __forceinline__ uint64_t logit_key(float z, uint32_t token) {
 __device__ __forceinline__ uint32_t logit_key_token(uint64_t key) {
     return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu);
 }
+// Inverse of float_order_key (-0.0 comes back as +0.0, which subtracts alike).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+// The logit a logit_key was made from.
+__device__ __forceinline__ float logit_key_value(uint64_t key) { return key_float((uint32_t)(key >> 32)); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, mask, kWave);
-    hi = __shfl_xor(hi, mask, kWave);
-    return ((uint64_t)hi << 32) | lo;
+// Wave reductions on the VALU: four DPP steps inside each 16-lane row (quad
+// permutations for distances 1 and 2, the half-row and row mirrors to join 4- and
+// 8-lane groups), then the row swaps permlane16 (l <-> l^16) and permlane32
+// (l <-> l^32).  Each step combines a lane with a partner holding the other
+// group's result, so every lane ends with the full reduction; a pair computes
+// op(a, b) and op(b, a), which agree for max and for +.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+// Both values of a row swap: one is the lane's own, the other its partner's.
+__device__ __forceinline__ void swap16_u64(uint64_t v, uint64_t& a, uint64_t& b) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    a = ((uint64_t)hi[0] << 32) | lo[0];
+    b = ((uint64_t)hi[1] << 32) | lo[1];
+}
+__device__ __forceinline__ void swap32_u64(uint64_t v, uint64_t& a, uint64_t& b) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    a = ((uint64_t)hi[0] << 32) | lo[0];
+    b = ((uint64_t)hi[1] << 32) | lo[1];
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
+    uint64_t p, a, b;
+    p = dpp_u64<kDppXor1>(v); v = p > v ? p : v;
+    p = dpp_u64<kDppXor2>(v); v = p > v ? p : v;
+    p = dpp_u64<kDppHalfMirror>(v); v = p > v ? p : v;
+    p = dpp_u64<kDppMirror>(v); v = p > v ? p : v;
+    swap16_u64(v, a, b); v = a > b ? a : b;
+    swap32_u64(v, a, b); v = a > b ? a : b;
     return v;
 }
 
+__device__ __forceinline__ double u64_f64(uint64_t u) { return __longlong_as_double((long long)u); }
+__device__ __forceinline__ uint64_t f64_u64(double d) { return (uint64_t)__double_as_longlong(d); }
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    uint64_t a, b;
+    v += u64_f64(dpp_u64<kDppXor1>(f64_u64(v)));
+    v += u64_f64(dpp_u64<kDppXor2>(f64_u64(v)));
+    v += u64_f64(dpp_u64<kDppHalfMirror>(f64_u64(v)));
+    v += u64_f64(dpp_u64<kDppMirror>(f64_u64(v)));
+    swap16_u64(f64_u64(v), a, b); v = u64_f64(a) + u64_f64(b);
+    swap32_u64(f64_u64(v), a, b); v = u64_f64(a) + u64_f64(b);
     return v;
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v)));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Block-wide sum of one double per thread; every thread receives the total.

@@ -10,9 +10,12 @@
 
 namespace eagle {
 
+// Expand: vocabulary chunks per draft row, then a per-sequence merge.
+int expand_chunks(int vocab);
+size_t expand_workspace_bytes(const eagle_tree_cfg& cfg);
 hipError_t launch_expand(const eagle_tree_cfg& cfg, int layer, int rows, int cap,
                          const float* logits, const int32_t* root_token,
-                         const eagle_tree_state& st, hipStream_t stream);
+                         const eagle_tree_state& st, void* workspace, hipStream_t stream);
 
 hipError_t launch_rerank(const eagle_tree_cfg& cfg, int cap, const eagle_tree_state& st,
                          int32_t* kept, hipStream_t stream);

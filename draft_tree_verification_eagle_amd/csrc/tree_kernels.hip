@@ -1,5 +1,6 @@
-// Dynamic draft-tree kernels for gfx950: Expand (per draft row and per layer),
-// Rerank, and flatten + ancestor mask + positions.
+// Dynamic draft-tree kernels for gfx950: Expand (vocabulary chunks, then one
+// merge per sequence that also selects the next frontier), Rerank, and flatten +
+// ancestor mask + positions.
 //
 // Operations follow the EAGLE-2 page (news write-up of "EAGLE-2: Faster
 // Inference of Language Models with Dynamic Draft Trees"): its two-stage passage
@@ -13,128 +14,170 @@
 
 namespace eagle {
 
-// ---------------------------------------------------------------------------
-// K1: one workgroup per (draft row, sequence).  Pass 1 keeps each thread's best
-// KCAP (logit, token) keys in registers; every wave then emits its top-k by k
-// rounds of wave-wide maxima; the waves' lists are merged by an LDS bitonic sort.
-// Pass 2 sums exp(z - zmax) in fp64 (zmax = best key's logit) and rounds the
-// log once to fp32.  The k children are written at ids base + j*k + rank.
-// ---------------------------------------------------------------------------
-constexpr int kExpandThreads = 1024;
-constexpr int kExpandWaves = kExpandThreads / kWave;
 
-template <int KCAP>
-__global__ __launch_bounds__(kExpandThreads) void expand_rows_kernel(
-    const float* __restrict__ logits, int V, int rows, int k, int layer,
+// ---------------------------------------------------------------------------
+// K1a: one workgroup per (vocabulary chunk of kChunk tokens, draft row,
+// sequence).  The chunk's top-k keys (logit desc, token asc) by k rounds of a
+// block-wide maximum, each round's owner dropping its key; then the chunk's fp64
+// sum of exp(z - chunk max).
+// ---------------------------------------------------------------------------
+constexpr int kChunkThreads = 256;
+constexpr int kChunkPerThread = 8;
+constexpr int kChunk = kChunkThreads * kChunkPerThread;  // 2048 tokens
+
+__global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
+    const float* __restrict__ logits, int V, int rows, int k, int C, uint64_t* __restrict__ ckeys,
+    float* __restrict__ cmax, double* __restrict__ csum) {
+    __shared__ uint64_t s_best[2][kChunkThreads / kWave];
+    __shared__ uint64_t s_top[EAGLE_MAX_TOPK];
+    __shared__ double s_red[kChunkThreads / kWave];
+    const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const size_t row = (size_t)b * rows + j;
+    const float* z = logits + row * (size_t)V;
+    const int t0 = c * kChunk;
+    float zv[kChunkPerThread];
+    uint64_t key[kChunkPerThread];
+#pragma unroll
+    for (int i = 0; i < kChunkPerThread; ++i) {
+        const int t = t0 + i * kChunkThreads + tid;
+        zv[i] = t < V ? z[t] : 0.0f;
+        key[i] = t < V ? logit_key(zv[i], (uint32_t)t) : 0;
+    }
+    uint64_t* out = ckeys + (row * C + c) * (size_t)k;
+    uint64_t top = 0;
+    for (int r = 0; r < k; ++r) {
+        uint64_t loc = key[0];
+#pragma unroll
+        for (int i = 1; i < kChunkPerThread; ++i) loc = key[i] > loc ? key[i] : loc;
+        const uint64_t w = wave_max_u64(loc);
+        if (lane == 0) s_best[r & 1][wid] = w;
+        __syncthreads();  // alternate buffers: one barrier per round
+        uint64_t best = s_best[r & 1][0];
+#pragma unroll
+        for (int q = 1; q < kChunkThreads / kWave; ++q) best = s_best[r & 1][q] > best ? s_best[r & 1][q] : best;
+        if (best != 0) {
+#pragma unroll
+            for (int i = 0; i < kChunkPerThread; ++i)
+                if (key[i] == best) key[i] = 0;  // keys are unique: one owner
+        }
+        // 0: the chunk holds fewer than k tokens.  Kept in LDS and stored after the
+        // loop: a global store here would make every round's barrier wait for it.
+        if (tid == 0) s_top[r] = best;
+        if (r == 0) top = best;
+    }
+    const double m = (double)logit_key_value(top);
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kChunkPerThread; ++i)
+        if (t0 + i * kChunkThreads + tid < V) s += exp((double)zv[i] - m);
+    s = block_sum_f64(s, s_red);  // its barriers also publish s_top
+    if (tid < k) out[tid] = s_top[tid];
+    if (tid == 0) {
+        cmax[row * C + c] = (float)m;
+        csum[row * C + c] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K1b: one workgroup per sequence.  One wave per draft row merges the row's C
+// sorted chunk lists (head pointers over an LDS copy) into its top-k, forms
+// lse = log(sum_c csum_c * exp(cmax_c - max)) in fp64 rounded once to fp32, and
+// writes the k children at ids base + j*k + rank.  Then, below the last layer,
+// the new layer's nodes are sorted by (value desc, id asc) in LDS and the first
+// min(m, layer size) become the next frontier.  Advances n_nodes.
+// ---------------------------------------------------------------------------
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishWaves = kFinishThreads / kWave;
+constexpr int kMergeLdsKeys = 8192;  // 64 KB of chunk lists per pass
+
+__global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
+    int rows, int k, int C, int layer, int depth_total, const uint64_t* __restrict__ ckeys,
+    const float* __restrict__ cmax, const double* __restrict__ csum,
     const int32_t* __restrict__ root_token, int cap, int m, int32_t* __restrict__ token,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth, float* __restrict__ value,
-    const int32_t* __restrict__ frontier, const int32_t* __restrict__ n_nodes) {
-    constexpr int P = kExpandWaves * KCAP;  // power of two
-    __shared__ uint64_t cand[P];
-    __shared__ double red[kExpandWaves];
-    __shared__ float s_lse32;
-
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-    const float* z = logits + ((size_t)b * rows + j) * (size_t)V;
-    const int f = (layer == 1) ? 0 : frontier[(size_t)b * m + j];
+    int32_t* __restrict__ frontier, int32_t* __restrict__ n_nodes) {
+    __shared__ uint64_t lists[kMergeLdsKeys];
+    __shared__ uint64_t fkeys[EAGLE_MAX_LAYER_NODES];
+    __shared__ float s_val[EAGLE_MAX_LAYER_NODES];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
     const int base = (layer == 1) ? 1 : n_nodes[b];
-    const float fval = (layer == 1) ? 0.0f : value[(size_t)b * cap + f];
+    const int L = rows * k;
+    const int per_row = C * k;
+    int waves = kMergeLdsKeys / per_row;  // rows merged at once
+    if (waves > kFinishWaves) waves = kFinishWaves;
 
-    // Pass 1: per-thread sorted (descending) top-KCAP keys; 0 marks an empty slot.
-    uint64_t list[KCAP];
-#pragma unroll
-    for (int i = 0; i < KCAP; ++i) list[i] = 0;
-    for (int t = tid; t < V; t += kExpandThreads) {
-        const uint64_t key = logit_key(z[t], (uint32_t)t);
-        if (key > list[KCAP - 1]) {
-            list[KCAP - 1] = key;
-#pragma unroll
-            for (int i = KCAP - 1; i > 0; --i) {
-                if (list[i] > list[i - 1]) {
-                    const uint64_t x = list[i];
-                    list[i] = list[i - 1];
-                    list[i - 1] = x;
-                }
-            }
-        }
-    }
-    // Wave stage: k rounds of the wave maximum; the winning lane pops its head.
-    for (int r = 0; r < KCAP; ++r) {
-        uint64_t best = 0;
-        if (r < k) {
-            best = wave_max_u64(list[0]);
-            if (best != 0 && list[0] == best) {
-#pragma unroll
-                for (int i = 0; i < KCAP - 1; ++i) list[i] = list[i + 1];
-                list[KCAP - 1] = 0;
-            }
-        }
-        if (lane == 0) cand[wid * KCAP + r] = best;
-    }
-    __syncthreads();
-    lds_bitonic_sort_desc(cand, P);  // cand[0..k-1]: the row's top-k
-
-    // Pass 2: fp64 normaliser from the row maximum (the best key's logit).
-    const uint32_t top_tok = logit_key_token(cand[0]);
-    const float row_max = z[top_tok];
-    double s = 0.0;
-    for (int t = tid; t < V; t += kExpandThreads) s += exp((double)z[t] - (double)row_max);
-    s = block_sum_f64(s, red);
-    if (tid == 0) s_lse32 = (float)log(s);
-    __syncthreads();
-
-    if (layer == 1 && j == 0 && tid == 0) {
+    if (layer == 1 && tid == 0) {
         const size_t r0 = (size_t)b * cap;
         token[r0] = root_token[b];
         parent[r0] = -1;
         depth[r0] = 0;
         value[r0] = 0.0f;
     }
-    if (tid < k) {
-        const uint32_t tok = logit_key_token(cand[tid]);
-        const float shifted = z[tok] - row_max;  // fp32
-        const float logq = shifted - s_lse32;    // fp32
-        const float val = fval + logq;           // fp32
-        const size_t idx = (size_t)b * cap + base + (size_t)j * k + tid;
-        token[idx] = (int32_t)tok;
-        parent[idx] = f;
-        depth[idx] = layer;
-        value[idx] = val;
+    for (int j0 = 0; j0 < rows; j0 += waves) {
+        const int j = j0 + wid;
+        const bool active = wid < waves && j < rows;
+        uint64_t* mine = lists + wid * per_row;
+        const size_t row = (size_t)b * rows + j;
+        if (active)
+            for (int i = lane; i < per_row; i += kWave) mine[i] = ckeys[row * per_row + i];
+        __syncthreads();
+        if (active) {
+            // lane q owns chunks q and q + 64 (C <= 128)
+            int p0 = 0, p1 = 0;
+            uint64_t mykey = 0;
+            for (int r = 0; r < k; ++r) {
+                const uint64_t h0 = (lane < C && p0 < k) ? mine[lane * k + p0] : 0;
+                const uint64_t h1 = (lane + kWave < C && p1 < k) ? mine[(lane + kWave) * k + p1] : 0;
+                const uint64_t loc = h0 > h1 ? h0 : h1;
+                const uint64_t best = wave_max_u64(loc);
+                if (best != 0) {
+                    if (h0 == best) ++p0;
+                    else if (h1 == best) ++p1;
+                }
+                if (lane == r) mykey = best;
+            }
+            const uint64_t top = __shfl(mykey, 0, kWave);
+            const float row_max = logit_key_value(top);
+            double s = 0.0;
+            if (lane < C) s += csum[row * C + lane] * exp((double)cmax[row * C + lane] - (double)row_max);
+            if (lane + kWave < C)
+                s += csum[row * C + lane + kWave] * exp((double)cmax[row * C + lane + kWave] - (double)row_max);
+            s = wave_sum_f64(s);
+            const float lse32 = (float)log(s);
+            const int f = (layer == 1) ? 0 : frontier[(size_t)b * m + j];
+            const float fval = (layer == 1) ? 0.0f : value[(size_t)b * cap + f];
+            if (lane < k) {
+                const uint32_t tok = logit_key_token(mykey);
+                const float shifted = logit_key_value(mykey) - row_max;  // fp32
+                const float logq = shifted - lse32;                      // fp32
+                const float val = fval + logq;                           // fp32
+                const size_t idx = (size_t)b * cap + base + (size_t)j * k + lane;
+                token[idx] = (int32_t)tok;
+                parent[idx] = f;
+                depth[idx] = layer;
+                value[idx] = val;
+                s_val[j * k + lane] = val;
+            }
+        }
+        __syncthreads();  // the lists area is reused by the next pass; every frontier entry read
     }
-}
-
-// ---------------------------------------------------------------------------
-// K2: per sequence, the new layer's nodes sorted by (value desc, id asc) in LDS;
-// the first min(m, layer size) become the next frontier.  Advances n_nodes.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void frontier_kernel(int layer, int depth_total, int rows, int k,
-                                                         int m, int cap,
-                                                         const float* __restrict__ value,
-                                                         int32_t* __restrict__ frontier,
-                                                         int32_t* __restrict__ n_nodes) {
-    __shared__ uint64_t keys[EAGLE_MAX_LAYER_NODES];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int base = (layer == 1) ? 1 : n_nodes[b];
-    const int L = rows * k;
     if (layer < depth_total) {
         const int P = next_pow2(L);
-        for (int i = tid; i < P; i += blockDim.x) {
+        for (int i = tid; i < P; i += kFinishThreads) {
             uint64_t key = 0;
             if (i < L) {
                 const uint32_t id = (uint32_t)(base + i);
-                key = ((uint64_t)float_order_key(value[(size_t)b * cap + id]) << 32) |
-                      (uint64_t)(0xFFFFFFFFu - id);
+                key = ((uint64_t)float_order_key(s_val[i]) << 32) | (uint64_t)(0xFFFFFFFFu - id);
             }
-            keys[i] = key;
+            fkeys[i] = key;
         }
         __syncthreads();
-        lds_bitonic_sort_desc(keys, P);
+        lds_bitonic_sort_desc(fkeys, P);
         const int keep = L < m ? L : m;
-        for (int i = tid; i < keep; i += blockDim.x)
-            frontier[(size_t)b * m + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu));
+        for (int i = tid; i < keep; i += kFinishThreads)
+            frontier[(size_t)b * m + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fkeys[i] & 0xFFFFFFFFu));
     }
-    __syncthreads();
     if (tid == 0) n_nodes[b] = base + L;
 }
 
@@ -230,28 +273,41 @@ __global__ __launch_bounds__(64) void mask_kernel(int cap, int n, const int32_t*
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
+// Expand workspace: per (sequence, draft row, chunk) the chunk's k keys, its max
+// logit and its fp64 exp sum; draft rows <= m.
+struct ExpandWs {
+    size_t keys, max, sum, total;
+};
+static ExpandWs expand_ws(const eagle_tree_cfg& cfg) {
+    const size_t C = (size_t)expand_chunks(cfg.vocab);
+    const size_t cells = (size_t)cfg.batch * (size_t)(cfg.m > 0 ? cfg.m : 1) * C;
+    ExpandWs w;
+    w.keys = 0;
+    w.max = (cells * (size_t)cfg.topk * 8 + 255) & ~(size_t)255;
+    w.sum = w.max + ((cells * 4 + 255) & ~(size_t)255);
+    w.total = w.sum + cells * 8;
+    return w;
+}
+
+int expand_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
+size_t expand_workspace_bytes(const eagle_tree_cfg& cfg) { return expand_ws(cfg).total; }
+
 hipError_t launch_expand(const eagle_tree_cfg& cfg, int layer, int rows, int cap,
                          const float* logits, const int32_t* root_token,
-                         const eagle_tree_state& st, hipStream_t stream) {
-    const dim3 grid(rows, cfg.batch);
-    const int k = cfg.topk;
-    if (k <= 8) {
-        expand_rows_kernel<8><<<grid, kExpandThreads, 0, stream>>>(
-            logits, cfg.vocab, rows, k, layer, root_token, cap, cfg.m, st.token, st.parent,
-            st.depth, st.value, st.frontier, st.n_nodes);
-    } else if (k <= 16) {
-        expand_rows_kernel<16><<<grid, kExpandThreads, 0, stream>>>(
-            logits, cfg.vocab, rows, k, layer, root_token, cap, cfg.m, st.token, st.parent,
-            st.depth, st.value, st.frontier, st.n_nodes);
-    } else {
-        expand_rows_kernel<32><<<grid, kExpandThreads, 0, stream>>>(
-            logits, cfg.vocab, rows, k, layer, root_token, cap, cfg.m, st.token, st.parent,
-            st.depth, st.value, st.frontier, st.n_nodes);
-    }
+                         const eagle_tree_state& st, void* workspace, hipStream_t stream) {
+    const int C = expand_chunks(cfg.vocab), k = cfg.topk;
+    const ExpandWs w = expand_ws(cfg);
+    unsigned char* ws = (unsigned char*)workspace;
+    uint64_t* ckeys = (uint64_t*)(ws + w.keys);
+    float* cmax = (float*)(ws + w.max);
+    double* csum = (double*)(ws + w.sum);
+    expand_chunk_kernel<<<dim3(C, rows, cfg.batch), kChunkThreads, 0, stream>>>(logits, cfg.vocab, rows, k,
+                                                                               C, ckeys, cmax, csum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    frontier_kernel<<<cfg.batch, 1024, 0, stream>>>(layer, cfg.depth, rows, k, cfg.m, cap, st.value,
-                                                    st.frontier, st.n_nodes);
+    expand_finish_kernel<<<cfg.batch, kFinishThreads, 0, stream>>>(
+        rows, k, C, layer, cfg.depth, ckeys, cmax, csum, root_token, cap, cfg.m, st.token, st.parent,
+        st.depth, st.value, st.frontier, st.n_nodes);
     return hipGetLastError();
 }
 

@@ -36,9 +36,15 @@ struct RowStats {
 };
 
 // ---------------------------------------------------------------------------
-// K6
+// K6: one workgroup of 1024 threads per (row, sequence).  Wave 0 finds the row's
+// children with one ballot (flattened order = lane order).  Thread tid handles
+// tokens t = tid + 1024 * it; a 128-bit mask marks which of its iterations hold
+// a child token, so the fp64 pass tests one register bit per token.
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kRowMaskIters = 128;  // vocab <= 131072 uses the mask
+constexpr int kRowBatch = 32;       // tokens per thread loaded together
 
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     const float* __restrict__ target, int T, int V, const int32_t* __restrict__ flat_token,
@@ -46,42 +52,87 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     __shared__ int32_t s_kid_row[kKids];
     __shared__ int32_t s_kid_tok[kKids];
     __shared__ int s_nk;
-    __shared__ uint64_t s_key[kRowThreads / kWave];
-    __shared__ double s_red[kRowThreads / kWave];
+    __shared__ uint64_t s_key[kRowWaves];
+    __shared__ double s_red[kRowWaves];
     const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wid = tid / kWave;
     const float* z = target + ((size_t)b * T + i) * (size_t)V;
-    if (tid == 0) {
-        int nk = 0;
-        for (int j = 0; j < T && nk < kKids; ++j) {
-            if (flat_parent[(size_t)b * T + j] == i) {
-                s_kid_row[nk] = j;
-                s_kid_tok[nk] = flat_token[(size_t)b * T + j];
-                ++nk;
+    if (wid == 0) {
+        const bool kid = lane < T && flat_parent[(size_t)b * T + lane] == i;
+        const uint64_t bal = __ballot(kid);
+        const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+        if (kid && pos < kKids) {
+            s_kid_row[pos] = lane;
+            s_kid_tok[pos] = flat_token[(size_t)b * T + lane];
+        }
+        if (lane == 0) s_nk = __popcll(bal) < kKids ? __popcll(bal) : kKids;
+    }
+    // Thread tid reads tokens t = tid + 1024 * it in unrolled batches of 32 (all
+    // loads of a batch in flight together); with vocab <= 32768 the single batch
+    // stays in registers for the second pass.
+    const int iters = (V + kRowThreads - 1) / kRowThreads;
+    float zr[kRowBatch];
+    uint64_t best = 0;
+    for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q) {
+            const int t = (it0 + q) * kRowThreads + tid;
+            zr[q] = t < V ? z[t] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q) {
+            const int t = (it0 + q) * kRowThreads + tid;
+            if (t < V) {
+                const uint64_t key = logit_key(zr[q], (uint32_t)t);
+                best = key > best ? key : best;
             }
         }
-        s_nk = nk;
-    }
-    uint64_t best = 0;
-    for (int t = tid; t < V; t += kRowThreads) {
-        const uint64_t key = logit_key(z[t], (uint32_t)t);
-        best = key > best ? key : best;
     }
     best = wave_max_u64(best);
     if (lane == 0) s_key[wid] = best;
     __syncthreads();
-    for (int w = 0; w < kRowThreads / kWave; ++w) best = s_key[w] > best ? s_key[w] : best;
+    for (int w = 0; w < kRowWaves; ++w) best = s_key[w] > best ? s_key[w] : best;
     const int amax = (int)logit_key_token(best);
-    const float zmax = z[amax];
+    const float zmax = logit_key_value(best);
     const int nk = s_nk;
     RowStats* out = stats + (size_t)b * T + i;
     if (temperature > 0.0f) {
         const double temp = (double)temperature;
+        const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
         double s = 0.0;
-        for (int t = tid; t < V; t += kRowThreads) {
-            bool kid = false;
-            for (int c = 0; c < nk; ++c) kid |= (s_kid_tok[c] == t);
-            if (!kid) s += exp(((double)z[t] - (double)zmax) / temp);
+        if (iters <= kRowMaskIters) {
+            uint64_t km0 = 0, km1 = 0;  // bit it: token tid + 1024 * it is a child
+            for (int c = 0; c < nk; ++c) {
+                const int tok = s_kid_tok[c];
+                if (tok % kRowThreads == tid) {
+                    const int it = tok / kRowThreads;
+                    if (it < 64) km0 |= 1ull << it; else km1 |= 1ull << (it - 64);
+                }
+            }
+            for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
+                if (iters > kRowBatch) {
+#pragma unroll
+                    for (int q = 0; q < kRowBatch; ++q) {
+                        const int t = (it0 + q) * kRowThreads + tid;
+                        zr[q] = t < V ? z[t] : 0.0f;
+                    }
+                }
+                const uint32_t kb = (uint32_t)((it0 < 64 ? km0 >> it0 : km1 >> (it0 - 64)) & 0xFFFFFFFFull);
+#pragma unroll
+                for (int q = 0; q < kRowBatch; ++q) {
+                    const int t = (it0 + q) * kRowThreads + tid;
+                    if (t < V && !((kb >> q) & 1u)) {
+                        const double x = (double)zr[q] - (double)zmax;
+                        s += exp(unit_temp ? x : x / temp);
+                    }
+                }
+            }
+        } else {
+            for (int t = tid; t < V; t += kRowThreads) {
+                bool kid = false;
+                for (int c = 0; c < nk; ++c) kid |= (s_kid_tok[c] == t);
+                if (!kid) s += exp(((double)z[t] - (double)zmax) / temp);
+            }
         }
         s = block_sum_f64(s, s_red);
         if (tid < nk) out->kid_e[tid] = exp(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
@@ -99,6 +150,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
 // K7
 // ---------------------------------------------------------------------------
 constexpr int kWalkThreads = 1024;
+constexpr int kMaxDepth = 255;  // the library's depth limit
 
 // Exclusive block prefix sum of one uint64 per thread (exact, order-free);
 // returns the thread's exclusive prefix and the block total.  Contains
@@ -136,92 +188,173 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
     float temperature, uint64_t seed, uint64_t step, const RowStats* __restrict__ stats,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_path,
     int32_t* __restrict__ out_tokens) {
+    __shared__ RowStats s_rs[EAGLE_MAX_TREE_ROWS];
+    __shared__ int32_t s_tok[EAGLE_MAX_TREE_ROWS];
+    __shared__ int32_t s_path[kMaxDepth];      // depth <= 255: accepted rows, -1 padded
+    __shared__ int32_t s_out[kMaxDepth + 1];   // accepted tokens then the bonus, -1 padded
     __shared__ int s_bonus_row, s_len;
     __shared__ int32_t s_removed[kKids];
     __shared__ int s_n_removed;
     __shared__ uint64_t s_wave[kWalkThreads / kWave];
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
     const bool sampled = temperature > 0.0f;
-    const RowStats* rs = stats + (size_t)b * T;
-    int32_t* path = accept_path + (size_t)b * depth;
-    int32_t* outt = out_tokens + (size_t)b * (depth + 1);
 
-    if (tid == 0) {
-        for (int d = 0; d < depth; ++d) path[d] = -1;
-        for (int d = 0; d <= depth; ++d) outt[d] = -1;
+    // the row statistics and tokens of this sequence, in one round trip
+    {
+        static_assert(sizeof(RowStats) % 8 == 0, "copied as 8-byte words");
+        const uint64_t* src = (const uint64_t*)(stats + (size_t)b * T);
+        uint64_t* dst = (uint64_t*)s_rs;
+        const int words = T * (int)(sizeof(RowStats) / 8);
+        for (int w = tid; w < words; w += kWalkThreads) dst[w] = src[w];
+        if (tid < T) s_tok[tid] = flat_token[(size_t)b * T + tid];
+        if (tid < depth) s_path[tid] = -1;
+        if (tid <= depth) s_out[tid] = -1;
+    }
+    __syncthreads();
+
+    // The walk, by wave 0: lane c evaluates child c of the current row.  The
+    // sequential rule takes the first child (flattened order) whose test passes,
+    // and child c's test depends only on c (the children before it are the ones
+    // already removed), so the lowest set bit of the ballot is that child.
+    if (tid < kWave) {
         int cur = 0, len = 0;
         while (true) {
-            const RowStats& R = rs[cur];
+            const RowStats& R = s_rs[cur];
+            const int nk = R.n_kids;
             int next = -1;
-            if (len < depth) {
-                if (!sampled) {
-                    for (int c = 0; c < R.n_kids; ++c)
-                        if (flat_token[(size_t)b * T + R.kid_row[c]] == R.argmax) { next = R.kid_row[c]; break; }
-                } else {
-                    for (int c = 0; c < R.n_kids; ++c) {
+            if (len < depth && nk > 0) {
+                bool pass = false;
+                if (lane < nk) {
+                    if (!sampled) {
+                        pass = s_tok[R.kid_row[lane]] == R.argmax;
+                    } else {
                         double denom = R.rest;
-                        for (int s2 = c; s2 < R.n_kids; ++s2) denom += R.kid_e[s2];
-                        const double ratio = R.kid_e[c] / denom;
-                        const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)c);
-                        if (u < ratio) { next = R.kid_row[c]; break; }
+                        for (int c = lane; c < nk; ++c) denom += R.kid_e[c];
+                        const double ratio = R.kid_e[lane] / denom;
+                        const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)lane);
+                        pass = u < ratio;
                     }
                 }
+                const uint64_t bal = __ballot(pass);
+                if (bal) next = R.kid_row[__ffsll((unsigned long long)bal) - 1];
             }
             if (next >= 0) {
-                path[len] = next;
-                outt[len] = flat_token[(size_t)b * T + next];
+                if (lane == 0) {
+                    s_path[len] = next;
+                    s_out[len] = s_tok[next];
+                }
                 ++len;
                 cur = next;
                 continue;
             }
-            if (!sampled) outt[len] = R.argmax;
-            // every child of the final row was tested and rejected (none when it is a leaf)
-            const int nrem = (len < depth) ? R.n_kids : 0;
-            for (int c = 0; c < nrem; ++c) s_removed[c] = flat_token[(size_t)b * T + R.kid_row[c]];
-            s_n_removed = nrem;
-            s_bonus_row = cur;
-            s_len = len;
+            if (lane == 0) {
+                if (!sampled) s_out[len] = R.argmax;
+                s_bonus_row = cur;
+                s_len = len;
+                // every child of the final row was tested and rejected (none when it is a leaf)
+                s_n_removed = (len < depth) ? nk : 0;
+            }
+            if (len < depth && lane < nk) s_removed[lane] = s_tok[R.kid_row[lane]];
             break;
         }
-        accept_len[b] = s_len;
     }
-    if (!sampled) return;
     __syncthreads();
 
-    // Bonus draw: smallest t whose running residual mass exceeds u * total, the
-    // masses in 2^-48 fixed point.  Thread tid owns tokens [t0, t1); the integer
-    // intervals [prefix, prefix + mass) partition [0, total) exactly, so exactly
-    // one thread holds the crossing.
-    const int row = s_bonus_row, nrem = s_n_removed;
-    const float* z = target + ((size_t)b * T + row) * (size_t)V;
-    const double zmax = (double)rs[row].zmax, temp = (double)temperature;
-    const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
-    const int t0 = min(V, tid * chunk), t1 = min(V, t0 + chunk);
-    uint64_t cs = 0;
-    for (int t = t0; t < t1; ++t) {
-        bool rem = false;
-        for (int c = 0; c < nrem; ++c) rem |= (s_removed[c] == t);
-        if (!rem) cs += fixed_mass(exp(((double)z[t] - zmax) / temp));
-    }
-    uint64_t total = 0;
-    const uint64_t prefix = block_exclusive_scan_u64(cs, s_wave, &total);
-    const Philox4x32 word = philox4x32_10(Philox4x32{kBonusSlot, (uint32_t)row, (uint32_t)b, (uint32_t)step},
-                                          (uint32_t)seed, (uint32_t)(seed >> 32));
-    const uint64_t u24 = (uint64_t)(word.c0 >> 8);
-    const uint64_t goal = __umul64hi(total, u24 << 40);  // floor(total * u24 / 2^24)
-    if (cs > 0 && prefix <= goal && goal < prefix + cs) {
-        uint64_t run = prefix;
-        for (int t = t0; t < t1; ++t) {
-            bool rem = false;
-            for (int c = 0; c < nrem; ++c) rem |= (s_removed[c] == t);
-            if (rem) continue;
-            run += fixed_mass(exp(((double)z[t] - zmax) / temp));
-            if (run > goal) {
-                outt[s_len] = t;
-                break;
+    if (sampled) {
+        // Bonus draw: smallest t whose running residual mass exceeds u * total, the
+        // masses in 2^-48 fixed point.  Thread tid owns tokens [t0, t1); the integer
+        // intervals [prefix, prefix + mass) partition [0, total) exactly, so exactly
+        // one thread holds the crossing.
+        const int row = s_bonus_row, nrem = s_n_removed;
+        const float* z = target + ((size_t)b * T + row) * (size_t)V;
+        const double zmax = (double)s_rs[row].zmax, temp = (double)temperature;
+        const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
+        const int chunk = (V + kWalkThreads - 1) / kWalkThreads;
+        const int t0 = min(V, tid * chunk), t1 = min(V, t0 + chunk);
+        const Philox4x32 word = philox4x32_10(Philox4x32{kBonusSlot, (uint32_t)row, (uint32_t)b, (uint32_t)step},
+                                              (uint32_t)seed, (uint32_t)(seed >> 32));
+        const uint64_t u24 = (uint64_t)(word.c0 >> 8);
+        uint64_t total = 0;
+        if (chunk <= 32) {
+            // masses kept in registers; removed tokens marked in a 32-bit mask
+            uint32_t rm = 0;
+            for (int c = 0; c < nrem; ++c) {
+                const int d = s_removed[c] - t0;
+                if (d >= 0 && d < t1 - t0) rm |= 1u << d;
+            }
+            uint64_t mass[32];
+            uint64_t cs = 0;
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                mass[q] = 0;
+                if (t0 + q < t1 && !((rm >> q) & 1u)) {
+                    const double x = (double)z[t0 + q] - zmax;
+                    mass[q] = fixed_mass(exp(unit_temp ? x : x / temp));
+                }
+                cs += mass[q];
+            }
+            const uint64_t prefix = block_exclusive_scan_u64(cs, s_wave, &total);
+            const uint64_t goal = __umul64hi(total, u24 << 40);  // floor(total * u24 / 2^24)
+            if (cs > 0 && prefix <= goal && goal < prefix + cs) {
+                uint64_t run = prefix;
+                int hit = -1;
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    run += mass[q];
+                    if (hit < 0 && run > goal) hit = q;
+                }
+                s_out[s_len] = t0 + hit;
+            }
+        } else {
+            // chunks up to 256 tokens: removed tokens marked in a 256-bit mask, the
+            // owner recomputes its masses
+            uint64_t rm[4] = {0, 0, 0, 0};
+            for (int c = 0; c < nrem; ++c) {
+                const int d = s_removed[c] - t0;
+                if (d >= 0 && d < t1 - t0) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        if ((d >> 6) == w) rm[w] |= 1ull << (d & 63);
+                }
+            }
+            uint64_t cs = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int a0 = t0 + 64 * w;
+                for (int q = 0; q < 64 && a0 + q < t1; ++q)
+                    if (!((rm[w] >> q) & 1ull)) {
+                        const double x = (double)z[a0 + q] - zmax;
+                        cs += fixed_mass(exp(unit_temp ? x : x / temp));
+                    }
+            }
+            const uint64_t prefix = block_exclusive_scan_u64(cs, s_wave, &total);
+            const uint64_t goal = __umul64hi(total, u24 << 40);  // floor(total * u24 / 2^24)
+            if (cs > 0 && prefix <= goal && goal < prefix + cs) {
+                uint64_t run = prefix;
+                bool done = false;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int a0 = t0 + 64 * w;
+                    for (int q = 0; q < 64 && a0 + q < t1 && !done; ++q) {
+                        if ((rm[w] >> q) & 1ull) continue;
+                        const double x = (double)z[a0 + q] - zmax;
+                        run += fixed_mass(exp(unit_temp ? x : x / temp));
+                        if (run > goal) {
+                            s_out[s_len] = a0 + q;
+                            done = true;
+                        }
+                    }
+                }
             }
         }
+        __syncthreads();
     }
+    // results, written once
+    int32_t* path = accept_path + (size_t)b * depth;
+    int32_t* outt = out_tokens + (size_t)b * (depth + 1);
+    if (tid < depth) path[tid] = s_path[tid];
+    if (tid <= depth) outt[tid] = s_out[tid];
+    if (tid == 0) accept_len[b] = s_len;
 }
 
 // ---------------------------------------------------------------------------

@@ -30,6 +30,8 @@ class VerifyStep:
             raise ValueError("capacity mismatch between library and workload shapes")
         i32 = dict(dtype=torch.int32, device=device)
         self.state = eb.TreeState.allocate(self.cfg, device)
+        ews = eb.eagle_tree_expand_workspace(self.cfg)
+        self.expand_ws = torch.zeros(max(ews, 1), dtype=torch.uint8, device=device)
         self.kept = torch.zeros((B, max(w.n, 1)), **i32)
         lens = w.ctx_lens() if ctx_lens is None else np.asarray(ctx_lens, dtype=np.int32)
         self.ctx_lens_np = lens
@@ -79,7 +81,8 @@ class VerifyStep:
     # ---- stages -----------------------------------------------------------
     def tree(self, stream=None):
         for layer in range(1, self.w.depth + 1):
-            eb.eagle_tree_expand(self.cfg, layer, self.draft_layers[layer - 1], self.root, self.state, stream)
+            eb.eagle_tree_expand(self.cfg, layer, self.draft_layers[layer - 1], self.root, self.state,
+                                 self.expand_ws, stream)
         if self.w.n > 0:
             eb.eagle_tree_rerank(self.cfg, self.state, self.kept, stream)
         eb.eagle_tree_mask(self.cfg, self.state, self.kept, self.ctx_len, self.flat_token, self.flat_parent,

@@ -61,6 +61,7 @@ typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 #define EAGLE_MAX_LAYER_NODES 1024 /* m * topk: nodes created in one layer */
 #define EAGLE_MAX_CAPACITY 4096    /* tree nodes incl. the root after `depth` layers */
 #define EAGLE_MAX_BATCH 1024
+#define EAGLE_MAX_VOCAB 262144    /* draft and target vocabulary size */
 
 /* Tree parameters, identical for every sequence of the batch.
  *   depth : draft layers below the root (>= 1); at most `depth` tokens are accepted
@@ -101,10 +102,16 @@ int32_t eagle_tree_frontier_rows(const eagle_tree_cfg* cfg, int32_t layer);
  * subtraction / addition.  Then, when layer < depth, frontier := the
  * min(m, |new layer|) new nodes of highest value (ties: lower id).
  * Layer 1 (re)initialises the tree from root_token [batch] (read only then).
- * Layers must be called in order 1..depth on the same stream. */
+ * Layers must be called in order 1..depth on the same stream.
+ * Workspace: eagle_tree_expand_workspace bytes of device memory owned by the
+ * caller, needing no initialisation; calls that share it must be stream-ordered.
+ * A null or smaller workspace is EAGLE_ERR_WORKSPACE; vocab > EAGLE_MAX_VOCAB is
+ * EAGLE_ERR_UNSUPPORTED. */
+size_t eagle_tree_expand_workspace(const eagle_tree_cfg* cfg);
+
 int eagle_tree_expand(const eagle_tree_cfg* cfg, int32_t layer, const float* draft_logits,
-                      const int32_t* root_token, const eagle_tree_state* state,
-                      hipStream_t stream);
+                      const int32_t* root_token, const eagle_tree_state* state, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* Rerank (EAGLE-2 page, two-stage passage): per sequence, the n non-root nodes
  * that come first in (value desc, depth asc, id asc), written to kept [batch][n]

@@ -77,6 +77,10 @@ def test_expand_validation(eb):
     L = eb.lib()
     st = _state(eb)
     good = eb.make_cfg(1, 100, 3, 4, 4, 10)
+    need = L.eagle_tree_expand_workspace(C.byref(good))
+    assert need > 0
+    call = lambda cfg, layer, logits=FAKE, root=FAKE, state=C.byref(st), ws=FAKE, nb=need: \
+        L.eagle_tree_expand(C.byref(cfg), layer, logits, root, state, ws, nb, None)
     for bad, code in [
         (eb.make_cfg(1, 100, 0, 4, 4, 10), eb.EAGLE_ERR_INVALID_ARG),    # depth 0
         (eb.make_cfg(1, 100, 3, 0, 4, 10), eb.EAGLE_ERR_INVALID_ARG),    # topk 0
@@ -85,17 +89,31 @@ def test_expand_validation(eb):
         (eb.make_cfg(1, 100, 3, 4, 4, 64), eb.EAGLE_ERR_UNSUPPORTED),    # T = 65 > 64
         (eb.make_cfg(1, 100, 3, 33, 4, 10), eb.EAGLE_ERR_UNSUPPORTED),   # topk > 32
         (eb.make_cfg(1, 10000, 3, 32, 33, 10), eb.EAGLE_ERR_UNSUPPORTED),  # m*k > 1024
+        (eb.make_cfg(1, 262145, 3, 4, 4, 10), eb.EAGLE_ERR_UNSUPPORTED),   # vocab > 262144
         (eb.make_cfg(1, 100, 2, 2, 2, 10), eb.EAGLE_ERR_INVALID_ARG),    # n > 6 candidates
     ]:
-        assert L.eagle_tree_expand(C.byref(bad), 1, FAKE, FAKE, C.byref(st), None) == code
-    assert L.eagle_tree_expand(C.byref(good), 0, FAKE, FAKE, C.byref(st), None) == eb.EAGLE_ERR_INVALID_ARG
-    assert L.eagle_tree_expand(C.byref(good), 4, FAKE, FAKE, C.byref(st), None) == eb.EAGLE_ERR_INVALID_ARG
-    assert L.eagle_tree_expand(C.byref(good), 1, FAKE, None, C.byref(st), None) == eb.EAGLE_ERR_INVALID_ARG
-    assert L.eagle_tree_expand(C.byref(good), 1, FAKE, FAKE, None, None) == eb.EAGLE_ERR_INVALID_ARG
+        assert call(bad, 1) == code
+    assert call(good, 0) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(good, 4) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(good, 1, root=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(good, 1, state=None) == eb.EAGLE_ERR_INVALID_ARG
     nul = eb.TreeStateC(FAKE, 0, FAKE, FAKE, FAKE, FAKE)
-    assert L.eagle_tree_expand(C.byref(good), 2, FAKE, FAKE, C.byref(nul), None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(good, 2, state=C.byref(nul)) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(good, 1, ws=None) == eb.EAGLE_ERR_WORKSPACE
+    assert call(good, 1, nb=need - 1) == eb.EAGLE_ERR_WORKSPACE
     empty = eb.make_cfg(0, 100, 3, 4, 4, 10)
-    assert L.eagle_tree_expand(C.byref(empty), 1, None, FAKE, C.byref(st), None) == eb.EAGLE_OK
+    assert call(empty, 1, logits=None, ws=None, nb=0) == eb.EAGLE_OK
+
+
+def test_expand_workspace_grows_with_vocab_batch_and_width(eb):
+    L = eb.lib()
+    ws = lambda *c: L.eagle_tree_expand_workspace(C.byref(eb.make_cfg(*c)))
+    a = ws(1, 32000, 6, 10, 10, 60)
+    assert a > 0
+    assert ws(1, 64000, 6, 10, 10, 60) > a      # more vocabulary chunks
+    assert ws(4, 32000, 6, 10, 10, 60) > a      # more sequences
+    assert ws(1, 32000, 6, 10, 20, 60) > a      # more draft rows per layer
+    assert ws(1, 262145, 6, 10, 10, 60) == 0    # unsupported configuration
 
 
 def test_rerank_and_mask_validation(eb):
