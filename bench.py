@@ -16,13 +16,17 @@ The JSON line carries:
   roofline  tree-attention HBM bandwidth: algorithmic bytes per launch (K + V of
             the ctx + T rows of every KV head, plus Q and O) / average launch
             time measured with HIP events on the launch stream, against the
-            8 TB/s HBM peak
-  cpu_baseline  the CPU oracle on a bounded sample (tree + 1 attention layer +
-            verify, single thread), scaled to one full step
+            8 TB/s HBM peak.  A launch is one eagle_tree_attention call: the
+            main kernel and its partial-merge kernel.  `traffic` (HBM bytes per
+            launch from FETCH_SIZE / WRITE_SIZE counters, scaled by a copy of known
+            size) is read from the committed counter summary when present.
+  cpu_baseline  the CPU oracle on a bounded sample (tree + 8 attention layers +
+            verify, single thread, about 10 s), scaled to one full step
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,22 +52,26 @@ def attention_bytes_per_launch(w) -> int:
     return kv + qo
 
 
-def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed):
-    """Oracle timing on a bounded sample: full tree + one attention layer + one
-    verification, single-threaded, scaled to the full step (layers x layer time)."""
+def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 8):
+    """Oracle timing on a bounded sample: full tree + `layers` distinct attention
+    layers + one verification, single-threaded, scaled to the full step
+    (tree + w.layers x mean layer time + verify)."""
     import oracle
     from draft_tree_verification_eagle_amd import workload as wl
-    import torch
 
     b = 0
     t0 = time.perf_counter()
     tree, kept, flat = oracle.build_tree(vs_draft[b], int(vs_root[b]), w.depth, w.topk, w.m, w.n, w.ctx)
     t_tree = time.perf_counter() - t0
-    q, k, v, off, total = wl.attention_inputs(w, 0, device="cpu")
-    qf = q[0].float().numpy(); kf = k.float().numpy(); vf = v.float().numpy()
-    t0 = time.perf_counter()
-    oracle.attention(qf, kf, vf, flat["mask"], w.ctx)
-    t_layer = time.perf_counter() - t0
+    layers = max(1, min(layers, w.layers))
+    t_layers = 0.0
+    for layer in range(layers):
+        q, k, v, off, total = wl.attention_inputs(w, layer, device="cpu")
+        qf = q[0].float().numpy(); kf = k.float().numpy(); vf = v.float().numpy()
+        t0 = time.perf_counter()
+        oracle.attention(qf, kf, vf, flat["mask"], w.ctx)
+        t_layers += time.perf_counter() - t0
+    t_layer = t_layers / layers
     t0 = time.perf_counter()
     if temperature > 0:
         oracle.verify_sampled(target[b], flat["flat_token"], flat["flat_parent"], w.depth, temperature, seed, 0, 0)
@@ -72,8 +80,9 @@ def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed):
     t_verify = time.perf_counter() - t0
     t_step = t_tree + w.layers * t_layer + t_verify
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"tree build + 1 of {w.layers} attention layers (fp64) + 1 verification, one thread; "
-                      f"step time = tree {t_tree:.3f}s + {w.layers} x layer {t_layer:.2f}s + verify {t_verify:.3f}s",
+            "sample": f"tree build + {layers} of {w.layers} attention layers (fp64, {t_layers:.1f}s) + 1 verification, "
+                      f"one thread; step time = tree {t_tree:.3f}s + {w.layers} x layer {t_layer:.2f}s + verify "
+                      f"{t_verify:.4f}s (the oracle evaluates only the rows its walk visits)",
             "oracle_attention_GBps": attention_bytes_per_launch(w) / t_layer / 1e9}
 
 
@@ -85,6 +94,9 @@ def main():
     ap.add_argument("--config", default="llama2_13b")
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB device to device 3 times (a plain copy kernel of "
+                         "known size whose FETCH_SIZE / WRITE_SIZE counters scale the attention's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
@@ -164,13 +176,25 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms_per_launch = e0.elapsed_time(e1) / (5 * n_attn)
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
     bytes_launch = attention_bytes_per_launch(w)
     achieved = bytes_launch / (ms_per_launch * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
+        # counters taken on an older kernel source do not describe this one
         try:
-            traffic = json.load(open(TRAFFIC_FILE)).get("bytes_per_launch")
-        except Exception:
+            rec = json.load(open(TRAFFIC_FILE))
+            src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+            if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+                traffic = rec["bytes_per_launch"]
+        except (OSError, KeyError, ValueError):
             traffic = None
 
     out = {
@@ -200,7 +224,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "tree_attn_bf16_kernel",
+            "kernel": "tree_attn_bf16_kernel + tree_attn_merge_kernel (one eagle_tree_attention call)",
             "bytes_per_launch": bytes_launch,
             "us_per_launch": round(ms_per_launch * 1e3, 3),
         },
