@@ -8,12 +8,13 @@
 //
 // BF16 path (head_dim 128): per sequence, a main kernel and a merge kernel.
 //  * Work unit = (KV head, group of 64 packed query rows); the packed rows of a KV
-//    head are its G = Hq/Hkv query heads x T tree rows.  The keys of all units
-//    (ctx + T each) form one linear list split evenly over 256 workgroups, one per
-//    CU, so every workgroup streams the same number of K/V bytes.  Workgroup
-//    index -> list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD
-//    takes one contiguous stretch, so the units that share K/V rows (GQA) read
-//    them through one L2.  A workgroup walks its stretch in tiles of <= 64 keys.
+//    head are its G = Hq/Hkv query heads x T tree rows.  The 64-key tiles of all
+//    units (ctx + T keys each) form one list, split over 256 workgroups, one per
+//    CU, on tile boundaries and weighted so that a workgroup spanning two units
+//    (two segments to merge and write) takes fewer tiles.  Workgroup index ->
+//    list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD takes one
+//    contiguous stretch, so the units that share K/V rows (GQA) read them
+//    through one L2.
 //  * K and V stream HBM -> LDS by direct 16-byte global_load_lds (no register
 //    staging), four stages deep: three tiles (96 KB) in flight per CU while one
 //    is computed.  Each load instruction covers 1 KB of contiguous rows.  Every
@@ -170,11 +171,47 @@ struct AttnArgs {
     float scale_log2;
 };
 
-// Workgroup (in list order) whose stretch [total*v/n, total*(v+1)/n) holds key x.
-__device__ __forceinline__ int stretch_of(int64_t x, int64_t total, int nwg) {
-    int v = (int)((x * nwg) / total);
-    while (v + 1 < nwg && total * (v + 1) / nwg <= x) ++v;
-    while (v > 0 && total * v / nwg > x) --v;
+// Work split.  Each unit's keys form nt = ceil(S / 64) tiles; the tiles are laid
+// on a cost line, unit after unit, each tile 4 cost steps long and each unit
+// preceded by kSegCost4 steps that stand for the fixed work of a segment (its
+// key-half merge and its output).  The line is cut into nwg equal stretches and a
+// workgroup takes the tiles that start in its stretch, so stretches end on tile
+// boundaries and a workgroup that spans two units takes fewer tiles.  Every
+// stretch is at least one tile plus one segment long, so each one holds a tile,
+// and the workgroups holding a unit's tiles are consecutive.
+constexpr int kSegCost4 = 2;
+struct Split {
+    int64_t W;      // cost steps per unit
+    int64_t Wt;     // cost steps in all
+    int nt;         // tiles per unit
+    int nwg;        // workgroups that take part
+};
+__device__ __forceinline__ Split make_split(int S, int units, int grid) {
+    Split sp;
+    sp.nt = (S + kTileKeys - 1) / kTileKeys;
+    sp.W = 4 * (int64_t)sp.nt + kSegCost4;
+    sp.Wt = (int64_t)units * sp.W;
+    const int64_t most = sp.Wt / (4 + kSegCost4);
+    sp.nwg = most < (int64_t)grid ? (most > 0 ? (int)most : 1) : grid;
+    return sp;
+}
+// Key-list position (unit * S + key) of the first tile starting at or after cost
+// step p; units * S past the last tile.
+__device__ __forceinline__ int64_t split_key(const Split& sp, int S, int64_t p) {
+    int64_t u = p / sp.W;
+    const int64_t r = p - u * sp.W;
+    int64_t t = r <= kSegCost4 ? 0 : (r - kSegCost4 + 3) / 4;
+    if (t >= sp.nt) {
+        ++u;
+        t = 0;
+    }
+    return u * S + t * kTileKeys;
+}
+// Workgroup (in list order) whose stretch [Wt*v/n, Wt*(v+1)/n) holds cost step p.
+__device__ __forceinline__ int stretch_of(int64_t p, int64_t total, int nwg) {
+    int v = (int)((p * nwg) / total);
+    while (v + 1 < nwg && total * (v + 1) / nwg <= p) ++v;
+    while (v > 0 && total * v / nwg > p) --v;
     return v;
 }
 
@@ -282,11 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const int S = ctx + T;
     const int64_t row0 = a.kv_row_off[0];
     const int units = a.Hkv * a.RG;
-    const int64_t total = (int64_t)units * S;
-    const int nwg = total < (int64_t)gridDim.x ? (int)total : (int)gridDim.x;
+    const Split sp = make_split(S, units, (int)gridDim.x);
     const int vwg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    if (vwg >= nwg) return;
-    const int64_t x_begin = total * vwg / nwg, x_end = total * (vwg + 1) / nwg;
+    if (vwg >= sp.nwg) return;
+    const int64_t x_begin = split_key(sp, S, sp.Wt * vwg / sp.nwg);
+    const int64_t x_end = split_key(sp, S, sp.Wt * (vwg + 1) / sp.nwg);
+    if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
 
     uint32_t off_full[4];
 #pragma unroll
@@ -596,10 +634,9 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
     const int unit = blockIdx.x;
     const int g = unit / a.RG, rg = unit - g * a.RG;
     const int S = a.ctx_len[0] + a.T;
-    const int64_t total = (int64_t)a.Hkv * a.RG * S;
-    const int nwg = total < (int64_t)grid_wg ? (int)total : grid_wg;
-    const int64_t U0 = (int64_t)unit * S;
-    const int vf = stretch_of(U0, total, nwg), vl = stretch_of(U0 + S - 1, total, nwg);
+    const Split sp = make_split(S, a.Hkv * a.RG, grid_wg);
+    const int64_t p0 = (int64_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
+    const int vf = stretch_of(p0, sp.Wt, sp.nwg), vl = stretch_of(p0 + 4 * (int64_t)(sp.nt - 1), sp.Wt, sp.nwg);
     if (vf == vl) return;  // written directly by the main kernel
     const int row = blockIdx.y * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
