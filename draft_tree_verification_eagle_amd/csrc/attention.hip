@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
     __shared__ uint32_t mslot[2 * kWave];
-    __shared__ float s_ml[2][2][kWave];
+    __shared__ float s_ml[2][2][2][kWave];  // [key half][query half][max, sum][lane]
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
     const int rb = wid & 1, ks = wid >> 1;
@@ -528,35 +528,46 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j][db], pb[j], oacc[db], 0, 0, 0);
 
         if (tc.seg_end) {
-            // ---- merge the two key halves: the second half leaves its rows,
-            // normalised by its own row sum, in fp16 (relative rounding 2^-11) in
-            // this stage's K area, which the scores consumed an iteration ago and
-            // which is refilled only after the next stage barrier ----
+            // ---- close the segment.  Each key half normalises its rows by its own
+            // row sum and hands the other half the 64 columns that half finishes
+            // (fp16, relative rounding 2^-11) through this stage's K area, dead
+            // since the scores of this tile.  Each wave then combines 32 rows x 64
+            // columns, stages them row-major in this stage's V area, and all four
+            // waves store whole 256-byte rows.  The stage is refilled only after
+            // the next stage barrier. ----
             // Without a next tile no stage barrier has passed since the scores of
             // this tile were read from K: wait for every wave before overwriting it.
             if (!has_next) barrier_lds();
+            unsigned char* const stg = smem + (it % kStages) * kStageBytes;
+            f16x4* const xch = reinterpret_cast<f16x4*>(stg);  // [2 sender ks][2 rb][2 db&1][4 qd][64 lanes]
+            unsigned char* const obuf = stg + kTileBytes;       // [64 rows][16 chunks of 16 B], swizzled
             const float lw = pair_sum(l_run);  // this wave's row sum over its keys
-            f16x4* mo = (f16x4*)st;            // [2 rb][4 db][4 q][64 lanes], 16 KB
-            if (ks == 1) {
+            {
                 const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
+                auto send = [&](const f32x16& acc, int jj) {
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         f16x4 w;
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) w[x] = (_Float16)(oacc[db][4 * qd + x] * inv);
-                        mo[((rb * 4 + db) * 4 + qd) * kWave + lane] = w;
+                        for (int x = 0; x < 4; ++x) w[x] = (_Float16)(acc[4 * qd + x] * inv);
+                        xch[(((ks * 2 + rb) * 2 + jj) * 4 + qd) * kWave + lane] = w;
                     }
-                s_ml[rb][0][lane] = m_run;
-                s_ml[rb][1][lane] = lw;
+                };
+                if (ks == 0) {  // the other half finishes columns 64..127
+                    send(oacc[2], 0);
+                    send(oacc[3], 1);
+                } else {        // the other half finishes columns 0..63
+                    send(oacc[0], 0);
+                    send(oacc[1], 1);
+                }
+                s_ml[ks][rb][0][lane] = m_run;
+                s_ml[ks][rb][1][lane] = lw;
             }
             barrier_lds();
-            if (ks == 0) {
-                const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
-                const bool whole = from0_c && tc.key0 + tc.nkeys == S;
-                const int rp = rg * kUnitRows + qrow;
-                const float m1 = s_ml[rb][0][lane], l1 = s_ml[rb][1][lane];
+            const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
+            const bool whole = from0_c && tc.key0 + tc.nkeys == S;
+            {
+                const float m1 = s_ml[ks ^ 1][rb][0][lane], l1 = s_ml[ks ^ 1][rb][1][lane];
                 const float M = fmaxf(m_run, m1);
                 const float Mu = (M == -INFINITY) ? 0.0f : M;
                 const float a0 = __builtin_amdgcn_exp2f(m_run - Mu);
@@ -565,46 +576,87 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 // a row that sees none of this segment's keys has ltot = 0: its partial
                 // is all zeros, and its merge weight is zero
                 const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+                const int row = 32 * rb + l32;
+                // the other half's values for this wave's 64 columns, all read before
+                // any staging write (the two areas share a stage)
+                f16x4 o1[2][4];
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        o1[jj][qd] = xch[((((ks ^ 1) * 2 + rb) * 2 + jj) * 4 + qd) * kWave + lane];
+                // combine this wave's columns (block db) and stage them as 2-byte values:
+                // bf16 for the output, fp16 for a partial
+                auto finish = [&](const f32x16& acc, int db, auto tag) {
+                    using V4 = decltype(tag);
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const f16x4 o1 = mo[((rb * 4 + db) * 4 + qd) * kWave + lane];
+                        V4 w;
 #pragma unroll
                         for (int x = 0; x < 4; ++x)
-                            oacc[db][4 * qd + x] = (oacc[db][4 * qd + x] * a0 + (float)o1[x] * w1) * inv;
+                            w[x] = (acc[4 * qd + x] * a0 + (float)o1[db & 1][qd][x] * w1) * inv;
+                        const int c = (4 * db + qd) ^ (row & 15);
+                        *reinterpret_cast<V4*>(obuf + row * kRowBytes + c * 16 + h2 * 8) = w;
                     }
-                if (rp < a.G * T) {
+                };
+                if (whole) {
+                    if (ks == 0) {
+                        finish(oacc[0], 0, bf16x4{});
+                        finish(oacc[1], 1, bf16x4{});
+                    } else {
+                        finish(oacc[2], 2, bf16x4{});
+                        finish(oacc[3], 3, bf16x4{});
+                    }
+                } else {
+                    if (ks == 0) {
+                        finish(oacc[0], 0, f16x4{});
+                        finish(oacc[1], 1, f16x4{});
+                    } else {
+                        finish(oacc[2], 2, f16x4{});
+                        finish(oacc[3], 3, f16x4{});
+                    }
+                }
+                const int rp = rg * kUnitRows + qrow;
+                if (ks == 0 && h2 == 0 && rp < a.G * T) {
                     if (whole) {
-                        int i, hq;
-                        query_row(a, g, rp, i, hq);
-                        __bf16* orow = a.o + ((int64_t)i * a.Hq + hq) * kD;
-#pragma unroll
-                        for (int db = 0; db < 4; ++db)
-#pragma unroll
-                            for (int qd = 0; qd < 4; ++qd) {
-                                bf16x4 w;
-#pragma unroll
-                                for (int x = 0; x < 4; ++x) w[x] = (__bf16)oacc[db][4 * qd + x];
-                                *(bf16x4*)(orow + 32 * db + 8 * qd + 4 * h2) = w;
-                            }
-                        if (h2 == 0 && a.lse) a.lse[(int64_t)i * a.Hq + hq] = (M + log2f(ltot)) * kLn2;
+                        if (a.lse) {
+                            int i, hq;
+                            query_row(a, g, rp, i, hq);
+                            a.lse[(int64_t)i * a.Hq + hq] = (M + log2f(ltot)) * kLn2;
+                        }
                     } else {
                         const int64_t slot = (int64_t)tc.unit + vwg;
-                        _Float16* po = a.part_o + slot * (kUnitRows * kD) + (int64_t)qrow * kD;
+                        a.part_ml[slot * 128 + qrow] = M;
+                        a.part_ml[slot * 128 + 64 + qrow] = ltot;
+                    }
+                }
+            }
+            barrier_lds();
+            // ---- whole rows out: wave wid stores rows 16 wid .. 16 wid + 15 ----
+            {
+                u32x4 val[4];
 #pragma unroll
-                        for (int db = 0; db < 4; ++db)
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int row = 16 * wid + 4 * r4 + (lane >> 4);
+                    val[r4] = *reinterpret_cast<const u32x4*>(obuf + row * kRowBytes + (((lane & 15) ^ (row & 15)) << 4));
+                }
+                if (whole) {
 #pragma unroll
-                            for (int qd = 0; qd < 4; ++qd) {
-                                f16x4 w;
-#pragma unroll
-                                for (int x = 0; x < 4; ++x) w[x] = (_Float16)oacc[db][4 * qd + x];
-                                *(f16x4*)(po + 32 * db + 8 * qd + 4 * h2) = w;
-                            }
-                        if (h2 == 0) {
-                            a.part_ml[slot * 128 + qrow] = M;
-                            a.part_ml[slot * 128 + 64 + qrow] = ltot;
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int rp = rg * kUnitRows + 16 * wid + 4 * r4 + (lane >> 4);
+                        if (rp < a.G * T) {
+                            int i, hq;
+                            query_row(a, g, rp, i, hq);
+                            *reinterpret_cast<u32x4*>(a.o + ((int64_t)i * a.Hq + hq) * kD + 8 * (lane & 15)) = val[r4];
                         }
+                    }
+                } else {
+                    _Float16* const po = a.part_o + ((int64_t)tc.unit + vwg) * (kUnitRows * kD);
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int row = 16 * wid + 4 * r4 + (lane >> 4);
+                        if (rg * kUnitRows + row < a.G * T)
+                            *reinterpret_cast<u32x4*>(po + row * kD + 8 * (lane & 15)) = val[r4];
                     }
                 }
             }
