@@ -15,25 +15,30 @@
 //    list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD takes one
 //    contiguous stretch, so the units that share K/V rows (GQA) read them
 //    through one L2.
-//  * K and V stream HBM -> LDS by direct 16-byte global_load_lds (no register
-//    staging), four stages deep: three tiles (96 KB) in flight per CU while one
-//    is computed.  Each load instruction covers 1 KB of contiguous rows.  Every
-//    tile issues the same 8 loads per thread (the stage barriers count them):
-//    lanes for rows past a short tile re-read the tile's last row, which the
-//    softmax masks out and which costs no extra HBM traffic.  LDS rows use a
-//    16-byte chunk XOR swizzle that keeps the MFMA operand reads conflict-free.
-//  * Q stays in registers for a whole segment.  The first segment's Q is loaded
-//    directly; a later segment's Q rides into an LDS slot with its first tile.
-//  * 4 waves = 2 query halves x 2 key halves of a tile.  S^T = K Q^T and
-//    O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16; V^T operands come straight
-//    from the row-major V tile through ds_read_b64_tr_b16.  The key order inside
-//    the S^T block is permuted so each half-wave's probabilities are the PV
-//    operand's 8 consecutive keys, with no register shuffles.  Online softmax in
-//    fp32 (base 2) with a lazy reference max: O is rescaled only when a row's max
-//    grows by more than 2^8, so the common tile does no rescale; probabilities
-//    are rounded to bf16 for PV.  The MFMA accumulators live in VGPRs (the library
-//    is built with the VGPR form of MFMA), so the softmax and rescale read them
-//    without accumulator-register copies.
+//  * Six waves per workgroup: four compute, two only load.  K and V stream HBM ->
+//    LDS by direct 16-byte global_load_lds (no register staging), four stages
+//    deep, issued and waited for by the two loader waves alone (each issues half
+//    of every tile's 1 KB row blocks).  A wave that issues a burst of such loads
+//    stalls until the memory pipeline takes them, and one wave alone cannot keep
+//    enough of them in flight, so the computing waves never issue one and two
+//    loaders share the stream.  Every wave runs the same tile walk and meets the
+//    same barriers.  Lanes for rows past a short tile re-read the tile's last
+//    row, which the softmax masks out and which costs no extra HBM traffic.  LDS
+//    rows use a 16-byte chunk XOR swizzle that keeps the MFMA operand reads
+//    conflict-free.
+//  * Q stays in registers for a whole segment; each segment's Q rides into an
+//    LDS slot ahead of its first tile (or, when the slot is still busy, is loaded
+//    directly when that tile's scores are computed).
+//  * The 4 computing waves = 2 query halves x 2 key halves of a tile.  S^T = K Q^T
+//    and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16; V^T operands come
+//    straight from the row-major V tile through ds_read_b64_tr_b16.  The key
+//    order inside the S^T block is permuted so each half-wave's probabilities are
+//    the PV operand's 8 consecutive keys, with no register shuffles.  Online
+//    softmax in fp32 (base 2) with a lazy reference max: O is rescaled only when
+//    a row's max grows by more than 2^8, so the common tile does no rescale;
+//    probabilities are rounded to bf16 for PV.  The MFMA accumulators live in
+//    VGPRs (the library is built with the VGPR form of MFMA), so the softmax and
+//    rescale read them without accumulator-register copies.
 //  * A workgroup whose stretch holds a whole unit writes the output; otherwise
 //    it writes a partial: row max and row sum in fp32 and the normalised row in
 //    fp16 (relative rounding 2^-11, inside the bf16 output's own).  The merge
@@ -60,19 +65,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kTileKeys = 64;
 constexpr int kUnitRows = 64;
-constexpr int kThreads = 256;
+constexpr int kComputeWaves = 4;                     // 2 query halves x 2 key halves
+#ifndef EAGLE_LOADERS
+#define EAGLE_LOADERS 2
+#endif
+constexpr int kLoaders = EAGLE_LOADERS;              // waves that issue the loads
+constexpr int kThreads = (kComputeWaves + kLoaders) * 64;
 constexpr int kStages = 4;
 constexpr int kGridWG = 256;                         // one per CU, multiple of the 8 XCDs
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kTileKeys * kRowBytes;    // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;          // K tile | V tile
 constexpr int kQBytes = kUnitRows * kRowBytes;       // 16 KB
-constexpr int kKVLoads = 2 * kTileBytes / (kThreads * 16);  // 8 per thread per tile
+constexpr int kTileLoads = 2 * kTileBytes / (64 * 16) / kLoaders;  // per loader lane per tile (K and V)
+constexpr int kQLoads = kQBytes / (64 * 16) / kLoaders + 2;         // per loader lane (+ mask words)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised probability
 
-static_assert(kKVLoads == 8 && kStages == 4, "the stage barriers assume 8 loads per tile, 4 stages");
+static_assert(kStages == 4 && 16 % kLoaders == 0, "4 stages; the loaders split the 16 blocks of a tile evenly");
 
 // 16-byte chunk position of logical chunk c in LDS row r: c ^ swz(r).
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
@@ -124,21 +135,30 @@ __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
-__device__ __forceinline__ void barrier_vm16() { asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void barrier_vm24() { asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void barrier_vm8() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void barrier_vm0() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Barrier for LDS traffic only (leaves the K/V loads in flight).
+// Barrier for LDS traffic (the K/V loads stay in flight).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Stage barrier given the number of tiles fetched after the awaited one.
-__device__ __forceinline__ void barrier_after(int after) {
-    if (after >= 2) barrier_vm16(); else if (after == 1) barrier_vm8(); else barrier_vm0();
+// Loader wave: wait until at most `tiles_after` tiles' loads (0 or 1) are still
+// in flight; loads complete in issue order, so everything issued before them has
+// landed.
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void loader_wait(int tiles_after) {
+    if (tiles_after >= 1) vm_wait<kTileLoads>();
+    else vm_wait<0>();
 }
 
 // s_waitcnt vmcnt(0) as the compiler sees it: after this, registers filled by
 // ordinary loads count as complete, so no wait for them is carried into the
 // tile loop (where any vmcnt wait would also drain the K/V pipeline).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A lane value the compiler must treat as unknown here: addresses derived from it
+// in the rarely taken paths (segment starts and ends) are recomputed there instead
+// of being hoisted out of the tile loop, where they would only hold registers.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
@@ -254,26 +274,31 @@ __device__ __forceinline__ void query_row(const AttnArgs& a, int g, int rp, int&
     hq = g * a.G + gi;
 }
 
-// Direct-to-LDS loads of one tile's K and V rows: always 8 per thread.  Lane
-// offsets for a full tile are precomputed; for a short tile, rows past nkeys
-// re-read row nkeys - 1 (masked out by the softmax, no extra HBM traffic).
-__device__ __forceinline__ void issue_kv(const AttnArgs& a, const Tile& t, int64_t row0, unsigned char* st,
-                                         const uint32_t (&off_full)[4], int wid, int lane) {
+// Direct-to-LDS loads of one tile's K and V rows, all issued by the loader wave:
+// 16 blocks of 4 rows each for K and for V, 32 loads per lane.  In a full tile,
+// block b starts 1 KB * b in and off4[b & 3] is the lane's offset inside it; for a
+// short tile, rows past
+// nkeys re-read row nkeys - 1 (masked out by the softmax, no extra HBM traffic).
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const Tile& t, int64_t row0, unsigned char* st,
+                                          const uint32_t (&off4)[4], int li, int lane) {
+    // keep the wave's outstanding-load count within the 63 its counter holds
+    vm_wait<63 - kTileLoads>();
     const int g = t.unit / a.RG;
     const int64_t elt0 = ((int64_t)g * a.kv_rows_total + row0 + t.key0) * kD;
     const __bf16* kb = a.k + elt0;
     const __bf16* vb = a.v + elt0;
     if (t.nkeys == kTileKeys) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int blk = n * 4 + wid;  // 16 blocks of 4 rows
-            dma_b128_nt(kb, off_full[n], lds_u32(st + blk * 1024));
-            dma_b128_nt(vb, off_full[n], lds_u32(st + kTileBytes + blk * 1024));
+        for (int bi = 0; bi < 16 / kLoaders; ++bi) {
+            const int blk = bi * kLoaders + li;
+            // the block's 1 KB step goes into the scalar base, the lane part stays in 4 VGPRs
+            dma_b128_nt(kb + blk * 512, off4[blk & 3], lds_u32(st + blk * 1024));
+            dma_b128_nt(vb + blk * 512, off4[blk & 3], lds_u32(st + kTileBytes + blk * 1024));
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int blk = n * 4 + wid;
+        for (int bi = 0; bi < 16 / kLoaders; ++bi) {
+            const int blk = bi * kLoaders + li;
             const int lrow = blk * 4 + (lane >> 4);
             const int grow = lrow < t.nkeys ? lrow : t.nkeys - 1;
             const uint32_t off = (uint32_t)(grow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
@@ -283,20 +308,22 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, const Tile& t, int64
     }
 }
 
-// Direct-to-LDS loads of a unit's 64 packed Q rows and their mask words.
-__device__ __forceinline__ void issue_q(const AttnArgs& a, int unit, unsigned char* qslot, uint32_t* mslot,
-                                        int wid, int lane) {
+// Direct-to-LDS loads of a unit's 64 packed Q rows and their mask words, by the
+// loader wave: 16 + 2 loads per lane.
+__device__ __forceinline__ void load_q(const AttnArgs& a, int unit, unsigned char* qslot, uint32_t* mslot,
+                                       int li, int lane) {
+    vm_wait<63 - kQLoads>();  // at most 63 loads in flight
     const int g = unit / a.RG, rg = unit - g * a.RG;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int blk = n * 4 + wid;
+    for (int bi = 0; bi < 16 / kLoaders; ++bi) {
+        const int blk = bi * kLoaders + li;
         const int rho = blk * 4 + (lane >> 4);
         int i, hq;
         query_row(a, g, rg * kUnitRows + rho, i, hq);
         const uint32_t off = (uint32_t)((((int64_t)i * a.Hq + hq) * kD) * 2 + (((lane & 15) ^ swz(rho)) << 4));
         dma_b128(a.q, off, lds_u32(qslot + blk * 1024));
     }
-    if (wid == 0) {
+    if (li == 0) {
         int i, hq;
         query_row(a, g, rg * kUnitRows + lane, i, hq);
         const uint32_t* mw = (const uint32_t*)(a.mask + i);
@@ -305,33 +332,24 @@ __device__ __forceinline__ void issue_q(const AttnArgs& a, int unit, unsigned ch
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
-    __shared__ uint32_t mslot[2 * kWave];
-    __shared__ float s_ml[2][2][2][kWave];  // [key half][query half][max, sum][lane]
-
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-    const int rb = wid & 1, ks = wid >> 1;
+// The tile walk of one workgroup, for the loader wave (kLoader) or a computing
+// wave.  Both instantiations share every branch that reaches a barrier, so the
+// five waves always meet the same barriers in the same order.
+template <bool kLoader>
+__device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem, unsigned char* qslot,
+                                          uint32_t* mslot, float (*s_ml)[2][2][kWave], int wid, int lane,
+                                          int T, int ctx, int S, int64_t row0, int vwg, int64_t x_begin,
+                                          int64_t x_end) {
+    constexpr bool loader = kLoader;
+    const int rb = wid & 1, ks = (wid >> 1) & 1;
     const int l32 = lane & 31, h2 = lane >> 5;
-    const int T = a.T;
-    const int ctx = a.ctx_len[0];
-    const int S = ctx + T;
-    const int64_t row0 = a.kv_row_off[0];
-    const int units = a.Hkv * a.RG;
-    const Split sp = make_split(S, units, (int)gridDim.x);
-    const int vwg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    if (vwg >= sp.nwg) return;
-    const int64_t x_begin = split_key(sp, S, sp.Wt * vwg / sp.nwg);
-    const int64_t x_end = split_key(sp, S, sp.Wt * (vwg + 1) / sp.nwg);
-    if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
-
-    uint32_t off_full[4];
+    // lane offset inside a full tile's block b (rows 4b .. 4b + 3), without the
+    // block's own 1 KB * b: the lane's row in the block and its swizzled chunk,
+    // which depends on b only through b & 3
+    uint32_t off4[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int lrow = (n * 4 + wid) * 4 + (lane >> 4);
-        off_full[n] = (uint32_t)(lrow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
-    }
+    for (int j = 0; j < 4; ++j)
+        off4[j] = (uint32_t)((lane >> 4) * kRowBytes + (((lane & 15) ^ swz(j * 4 + (lane >> 4))) << 4));
 
     Walker w0;
     w0.x = x_begin;
@@ -353,35 +371,45 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         wait_direct_loads();
     };
 
-    // ---- prologue: tiles 0..2 in flight; a later segment's Q goes to the slot ----
+    // this lane's Q row and mask word from the Q slot
+    auto read_q_slot = [&]() {
+        const int qr = opaque(qrow), hh = opaque(h2);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int c = (2 * kk + hh) ^ swz(qr);
+            qcur[kk] = *(const bf16x8*)(qslot + qr * kRowBytes + c * 16);
+        }
+        mword_n = (uint64_t)mslot[qr] | ((uint64_t)mslot[kWave + qr] << 32);
+    };
+
+    // ---- prologue.  Every wave runs the same tile bookkeeping and barriers; only
+    // the loader issues and waits for loads. ----
     Walker wf = w0;           // next tile to fetch
     int nl = 0;               // tiles fetched so far
     int q_slot_tile = 0;      // tile whose Q is in (or on its way to) the Q slot
-    // The first segment's Q goes through the slot too, issued ahead of the first
-    // tiles so that its latency overlaps their streaming.
-    issue_q(a, w0.unit, qslot, mslot, wid, lane);
+    // The first segment's Q goes through the slot, issued ahead of the first tiles.
+    if (loader) load_q(a, w0.unit, qslot, mslot, wid - kComputeWaves, lane);
     // A later segment's Q rides with its first tile into the slot when the slot is
     // free; otherwise that tile loads its Q directly when its scores are computed.
     auto fetch = [&]() {
         const Tile t = peek(wf, x_begin, x_end, S);
-        issue_kv(a, t, row0, smem + (nl % kStages) * kStageBytes, off_full, wid, lane);
+        if (loader) load_tile(a, t, row0, smem + (nl % kStages) * kStageBytes, off4, wid - kComputeWaves, lane);
         if (t.seg_start && nl > 0 && q_slot_tile < 0) {
-            issue_q(a, t.unit, qslot, mslot, wid, lane);
+            if (loader) load_q(a, t.unit, qslot, mslot, wid - kComputeWaves, lane);
             q_slot_tile = nl;
         }
         advance(wf, t.nkeys, S);
         ++nl;
     };
-    for (int s = 0; s < kStages - 1 && wf.x < x_end; ++s) fetch();
-    // The Q loads were issued before the nl tiles' 8 * nl loads: wait for them only.
-    if (nl >= 3) barrier_vm24(); else if (nl == 2) barrier_vm16(); else barrier_vm8();
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const int c = (2 * kk + h2) ^ swz(qrow);
-        qcur[kk] = *(const bf16x8*)(qslot + qrow * kRowBytes + c * 16);
+    fetch();
+    if (wf.x < x_end) fetch();
+    if (loader) loader_wait(nl - 1);  // the Q slot and tile 0
+    barrier_lds();
+    if (wf.x < x_end) fetch();        // tile 2: its stage has not been used yet
+    if (!loader) {
+        read_q_slot();
     }
-    mword_n = (uint64_t)mslot[qrow] | ((uint64_t)mslot[kWave + qrow] << 32);
-    q_slot_tile = -1;  // free once every wave has passed the tile-0 barrier
+    q_slot_tile = -1;  // free once every wave has passed the next barrier
 
     const int krow = 32 * ks + key_of_row(l32);
     const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
@@ -400,12 +428,12 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         return acc;
     };
 
-    // ---- tile 0: wait, scores ----
-    barrier_after(nl - 1);
+    // ---- tile 0: scores ----
     Walker wn = w0;           // tile whose scores are computed next
     Tile tc = peek(wn, x_begin, x_end, S);
     advance(wn, tc.nkeys, S);
-    f32x16 sacc = scores(smem);
+    f32x16 sacc;
+    if (!loader) sacc = scores(smem);
     uint64_t mword_c = mword_n;
     bool from0_c = tc.key0 == 0;  // the current segment starts at the unit's first key
 
@@ -423,27 +451,27 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         Tile tn;
         bool from0_n = from0_c;
         if (has_next) {
-            barrier_after(nl - it - 2);  // tile it+1 has landed; tile it-1's stage is free
+            // tile it+1 has landed; tile it-1's stage is free
+            if (loader) loader_wait(nl - it - 2);
+            barrier_lds();
             if (wf.x < x_end) fetch();
             tn = peek(wn, x_begin, x_end, S);
             if (tn.seg_start) {
                 if (q_slot_tile == it + 1) {
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) {
-                        const int c = (2 * kk + h2) ^ swz(qrow);
-                        qcur[kk] = *(const bf16x8*)(qslot + qrow * kRowBytes + c * 16);
+                    if (!loader) {
+                        read_q_slot();
                     }
-                    mword_n = (uint64_t)mslot[qrow] | ((uint64_t)mslot[kWave + qrow] << 32);
                     q_slot_tile = -1;  // free once every wave has passed the next barrier
-                } else {
-                    load_q_direct(tn.unit);  // drains the K/V loads too: rare (short segments)
+                } else if (!loader) {
+                    load_q_direct(tn.unit);  // rare (short segments)
                 }
                 from0_n = tn.key0 == 0;
             }
         }
 
-        const unsigned char* st = smem + (it % kStages) * kStageBytes;
-        const unsigned char* sV = st + kTileBytes;
+        f32x16 snext;
+        if (!loader) {
+        const unsigned char* sV = smem + (it % kStages) * kStageBytes + kTileBytes;
 
         // ---- online softmax (base 2): lane = one query row, 16 of its keys ----
         // Raw scores; the scale (> 0) is applied inside the exponent.
@@ -500,7 +528,6 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             }
         }
         const unsigned char* sKn = smem + ((it + 1) % kStages) * kStageBytes;
-        f32x16 snext;
 #pragma unroll
         for (int e = 0; e < 16; ++e) snext[e] = 0.0f;
         float psum = 0.0f;
@@ -526,6 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[j][db], pb[j], oacc[db], 0, 0, 0);
+        }  // computing waves
 
         if (tc.seg_end) {
             // ---- close the segment.  Each key half normalises its rows by its own
@@ -542,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             f16x4* const xch = reinterpret_cast<f16x4*>(stg);  // [2 sender ks][2 rb][2 db&1][4 qd][64 lanes]
             unsigned char* const obuf = stg + kTileBytes;       // [64 rows][16 chunks of 16 B], swizzled
             const float lw = pair_sum(l_run);  // this wave's row sum over its keys
-            {
+            if (!loader) {
                 const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
                 auto send = [&](const f32x16& acc, int jj) {
 #pragma unroll
@@ -566,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             barrier_lds();
             const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
             const bool whole = from0_c && tc.key0 + tc.nkeys == S;
-            {
+            if (!loader) {
                 const float m1 = s_ml[ks ^ 1][rb][0][lane], l1 = s_ml[ks ^ 1][rb][1][lane];
                 const float M = fmaxf(m_run, m1);
                 const float Mu = (M == -INFINITY) ? 0.0f : M;
@@ -576,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 // a row that sees none of this segment's keys has ltot = 0: its partial
                 // is all zeros, and its merge weight is zero
                 const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-                const int row = 32 * rb + l32;
+                const int row = opaque(32 * rb + l32);
                 // the other half's values for this wave's 64 columns, all read before
                 // any staging write (the two areas share a stage)
                 f16x4 o1[2][4];
@@ -632,31 +660,32 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
                 }
             }
             barrier_lds();
-            // ---- whole rows out: wave wid stores rows 16 wid .. 16 wid + 15 ----
-            {
+            // ---- whole rows out: computing wave wid stores rows 16 wid .. 16 wid + 15 ----
+            if (!loader) {
+                const int ln = opaque(lane);
                 u32x4 val[4];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int row = 16 * wid + 4 * r4 + (lane >> 4);
-                    val[r4] = *reinterpret_cast<const u32x4*>(obuf + row * kRowBytes + (((lane & 15) ^ (row & 15)) << 4));
+                    const int row = 16 * wid + 4 * r4 + (ln >> 4);
+                    val[r4] = *reinterpret_cast<const u32x4*>(obuf + row * kRowBytes + (((ln & 15) ^ (row & 15)) << 4));
                 }
                 if (whole) {
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
-                        const int rp = rg * kUnitRows + 16 * wid + 4 * r4 + (lane >> 4);
+                        const int rp = rg * kUnitRows + 16 * wid + 4 * r4 + (ln >> 4);
                         if (rp < a.G * T) {
                             int i, hq;
                             query_row(a, g, rp, i, hq);
-                            *reinterpret_cast<u32x4*>(a.o + ((int64_t)i * a.Hq + hq) * kD + 8 * (lane & 15)) = val[r4];
+                            *reinterpret_cast<u32x4*>(a.o + ((int64_t)i * a.Hq + hq) * kD + 8 * (ln & 15)) = val[r4];
                         }
                     }
                 } else {
                     _Float16* const po = a.part_o + ((int64_t)tc.unit + vwg) * (kUnitRows * kD);
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
-                        const int row = 16 * wid + 4 * r4 + (lane >> 4);
+                        const int row = 16 * wid + 4 * r4 + (ln >> 4);
                         if (rg * kUnitRows + row < a.G * T)
-                            *reinterpret_cast<u32x4*>(po + row * kD + 8 * (lane & 15)) = val[r4];
+                            *reinterpret_cast<u32x4*>(po + row * kD + 8 * (ln & 15)) = val[r4];
                     }
                 }
             }
@@ -675,6 +704,36 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         mword_c = mword_n;
         from0_c = from0_n;
     }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
+    __shared__ uint32_t mslot[2 * kWave];
+    __shared__ float s_ml[2][2][2][kWave];  // [key half][query half][max, sum][lane]
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int T = a.T;
+    const int ctx = a.ctx_len[0];
+    const int S = ctx + T;
+    const int64_t row0 = a.kv_row_off[0];
+    const int units = a.Hkv * a.RG;
+    const Split sp = make_split(S, units, (int)gridDim.x);
+    const int vwg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (vwg >= sp.nwg) return;
+    const int64_t x_begin = split_key(sp, S, sp.Wt * vwg / sp.nwg);
+    const int64_t x_end = split_key(sp, S, sp.Wt * (vwg + 1) / sp.nwg);
+    if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
+
+    // waves 0..3 compute (query half, key half); wave 4 issues every K, V and Q
+    // load and waits for them, so no computing wave stalls on a load issue.  Both
+    // roles run the same tile walk and the same barriers.
+    if (wid >= kComputeWaves)
+        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end);
+    else
+        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end);
+
 }
 
 // ---------------------------------------------------------------------------
@@ -849,7 +908,7 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.kv_rows_total = d.kv_rows_total;
         a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
         a.scale_log2 = scale * kLog2e;
-        tree_attn_bf16_kernel<<<kGridWG, kThreads, 0, stream>>>(a);
+        tree_attn_bf16_kernel<<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + the loader
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         tree_attn_merge_kernel<<<dim3(d.n_kv_heads * RG, kUnitRows / 16), 256, 0, stream>>>(a, kGridWG);
