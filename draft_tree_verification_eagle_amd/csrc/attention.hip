@@ -15,12 +15,12 @@
 //    list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD takes one
 //    contiguous stretch, so the units that share K/V rows (GQA) read them
 //    through one L2.
-//  * Six waves per workgroup: four compute, two only load.  K and V stream HBM ->
+//  * Eight waves per workgroup: four compute, four only load.  K and V stream HBM ->
 //    LDS by direct 16-byte global_load_lds (no register staging), four stages
-//    deep, issued and waited for by the two loader waves alone (each issues half
-//    of every tile's 1 KB row blocks).  A wave that issues a burst of such loads
+//    deep, issued and waited for by the loader waves alone (each issues a quarter
+//    of every tile's 1 KB row blocks, K before V).  A wave that issues a burst of such loads
 //    stalls until the memory pipeline takes them, and one wave alone cannot keep
-//    enough of them in flight, so the computing waves never issue one and two
+//    enough of them in flight, so the computing waves never issue one and four
 //    loaders share the stream.  Every wave runs the same tile walk and meets the
 //    same barriers.  Lanes for rows past a short tile re-read the tile's last
 //    row, which the softmax masks out and which costs no extra HBM traffic.  LDS
@@ -67,7 +67,7 @@ constexpr int kTileKeys = 64;
 constexpr int kUnitRows = 64;
 constexpr int kComputeWaves = 4;                     // 2 query halves x 2 key halves
 #ifndef EAGLE_LOADERS
-#define EAGLE_LOADERS 2
+#define EAGLE_LOADERS 4
 #endif
 constexpr int kLoaders = EAGLE_LOADERS;              // waves that issue the loads
 constexpr int kThreads = (kComputeWaves + kLoaders) * 64;
@@ -288,23 +288,32 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const Tile& t, int6
     const __bf16* kb = a.k + elt0;
     const __bf16* vb = a.v + elt0;
     if (t.nkeys == kTileKeys) {
+        // K first, then V: the first tile's scores can start before its V lands.
+        // The block's 1 KB step goes into the scalar base, the lane part stays in 4 VGPRs.
 #pragma unroll
         for (int bi = 0; bi < 16 / kLoaders; ++bi) {
             const int blk = bi * kLoaders + li;
-            // the block's 1 KB step goes into the scalar base, the lane part stays in 4 VGPRs
             dma_b128_nt(kb + blk * 512, off4[blk & 3], lds_u32(st + blk * 1024));
+        }
+#pragma unroll
+        for (int bi = 0; bi < 16 / kLoaders; ++bi) {
+            const int blk = bi * kLoaders + li;
             dma_b128_nt(vb + blk * 512, off4[blk & 3], lds_u32(st + kTileBytes + blk * 1024));
         }
     } else {
+        uint32_t off[16 / kLoaders];
 #pragma unroll
         for (int bi = 0; bi < 16 / kLoaders; ++bi) {
-            const int blk = bi * kLoaders + li;
-            const int lrow = blk * 4 + (lane >> 4);
+            const int lrow = (bi * kLoaders + li) * 4 + (lane >> 4);
             const int grow = lrow < t.nkeys ? lrow : t.nkeys - 1;
-            const uint32_t off = (uint32_t)(grow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
-            dma_b128_nt(kb, off, lds_u32(st + blk * 1024));
-            dma_b128_nt(vb, off, lds_u32(st + kTileBytes + blk * 1024));
+            off[bi] = (uint32_t)(grow * kRowBytes + (((lane & 15) ^ swz(lrow)) << 4));
         }
+#pragma unroll
+        for (int bi = 0; bi < 16 / kLoaders; ++bi)
+            dma_b128_nt(kb, off[bi], lds_u32(st + (bi * kLoaders + li) * 1024));
+#pragma unroll
+        for (int bi = 0; bi < 16 / kLoaders; ++bi)
+            dma_b128_nt(vb, off[bi], lds_u32(st + kTileBytes + (bi * kLoaders + li) * 1024));
     }
 }
 
@@ -403,7 +412,13 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     };
     fetch();
     if (wf.x < x_end) fetch();
-    if (loader) loader_wait(nl - 1);  // the Q slot and tile 0
+    // the Q slot and tile 0's K; its V and tile 1 may still be in flight, since the
+    // first iteration's barrier waits for both.  A one-tile stretch has no such
+    // barrier: there everything must land here.
+    if (loader) {
+        if (nl > 1) vm_wait<kTileLoads / 2 + kTileLoads>();
+        else vm_wait<0>();
+    }
     barrier_lds();
     if (wf.x < x_end) fetch();        // tile 2: its stage has not been used yet
     if (!loader) {
