@@ -76,6 +76,33 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(r[0], r[1]);
+}
+
+// Wave maximum of 64-bit keys by 32-bit steps: the maximum high word, then, if one
+// lane alone holds it, that lane's key; otherwise the maximum low word among the
+// lanes holding it.  Equal to wave_max_u64 for any keys.
+__device__ __forceinline__ uint64_t wave_max_key_u64(uint64_t v) {
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mhi = wave_max_u32(hi);
+    const uint64_t holders = __ballot(hi == mhi);
+    if (__builtin_popcountll(holders) == 1) {
+        const int l = __builtin_ctzll(holders);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+        return ((uint64_t)mhi << 32) | lo;
+    }
+    const uint32_t mlo = wave_max_u32(hi == mhi ? (uint32_t)v : 0u);
+    return ((uint64_t)mhi << 32) | mlo;
+}
+
 __device__ __forceinline__ double u64_f64(uint64_t u) { return __longlong_as_double((long long)u); }
 __device__ __forceinline__ uint64_t f64_u64(double d) { return (uint64_t)__double_as_longlong(d); }
 

@@ -17,65 +17,94 @@ namespace eagle {
 
 // ---------------------------------------------------------------------------
 // K1a: one workgroup per (vocabulary chunk of kChunk tokens, draft row,
-// sequence).  The chunk's top-k keys (logit desc, token asc) by k rounds of a
-// block-wide maximum, each round's owner dropping its key; then the chunk's fp64
-// sum of exp(z - chunk max).
+// sequence); each wave owns 256 consecutive tokens of the chunk.  A wave takes its
+// top-k keys (logit desc, token asc) by k rounds of a wave maximum, the round's
+// owner dropping its key (no barriers), and the fp64 sum of exp(z - its max).
+// Wave 0 then merges the four sorted wave lists by rank into the chunk's top-k,
+// and rescales the wave sums to the chunk max.
 // ---------------------------------------------------------------------------
 constexpr int kChunkThreads = 256;
-constexpr int kChunkPerThread = 8;
-constexpr int kChunk = kChunkThreads * kChunkPerThread;  // 2048 tokens
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kChunkPerLane = 4;
+constexpr int kChunk = kChunkThreads * kChunkPerLane;  // 1024 tokens
 
 __global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
     const float* __restrict__ logits, int V, int rows, int k, int C, uint64_t* __restrict__ ckeys,
     float* __restrict__ cmax, double* __restrict__ csum) {
-    __shared__ uint64_t s_best[2][kChunkThreads / kWave];
-    __shared__ uint64_t s_top[EAGLE_MAX_TOPK];
-    __shared__ double s_red[kChunkThreads / kWave];
+    __shared__ uint64_t s_wl[kChunkWaves][EAGLE_MAX_TOPK];  // each wave's top-k, best first
+    __shared__ double s_ws[kChunkWaves];                     // each wave's sum of exp(z - wave max)
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
     const size_t row = (size_t)b * rows + j;
     const float* z = logits + row * (size_t)V;
-    const int t0 = c * kChunk;
-    float zv[kChunkPerThread];
-    uint64_t key[kChunkPerThread];
+    const int t0 = c * kChunk + wid * (kWave * kChunkPerLane);
+    float zv[kChunkPerLane];
+    uint64_t key[kChunkPerLane];
 #pragma unroll
-    for (int i = 0; i < kChunkPerThread; ++i) {
-        const int t = t0 + i * kChunkThreads + tid;
+    for (int i = 0; i < kChunkPerLane; ++i) {
+        const int t = t0 + i * kWave + lane;
         zv[i] = t < V ? z[t] : 0.0f;
         key[i] = t < V ? logit_key(zv[i], (uint32_t)t) : 0;
     }
-    uint64_t* out = ckeys + (row * C + c) * (size_t)k;
-    uint64_t top = 0;
+    // this wave's top-k: lane r ends holding the r-th key (0: fewer than k tokens)
+    uint64_t mine = 0;
     for (int r = 0; r < k; ++r) {
         uint64_t loc = key[0];
 #pragma unroll
-        for (int i = 1; i < kChunkPerThread; ++i) loc = key[i] > loc ? key[i] : loc;
-        const uint64_t w = wave_max_u64(loc);
-        if (lane == 0) s_best[r & 1][wid] = w;
-        __syncthreads();  // alternate buffers: one barrier per round
-        uint64_t best = s_best[r & 1][0];
-#pragma unroll
-        for (int q = 1; q < kChunkThreads / kWave; ++q) best = s_best[r & 1][q] > best ? s_best[r & 1][q] : best;
+        for (int i = 1; i < kChunkPerLane; ++i) loc = key[i] > loc ? key[i] : loc;
+        const uint64_t best = wave_max_key_u64(loc);
         if (best != 0) {
 #pragma unroll
-            for (int i = 0; i < kChunkPerThread; ++i)
+            for (int i = 0; i < kChunkPerLane; ++i)
                 if (key[i] == best) key[i] = 0;  // keys are unique: one owner
         }
-        // 0: the chunk holds fewer than k tokens.  Kept in LDS and stored after the
-        // loop: a global store here would make every round's barrier wait for it.
-        if (tid == 0) s_top[r] = best;
-        if (r == 0) top = best;
+        if (lane == r) mine = best;
     }
-    const double m = (double)logit_key_value(top);
+    const uint64_t wtop = __shfl(mine, 0, kWave);
     double s = 0.0;
+    if (wtop != 0) {
+        const double wm = (double)logit_key_value(wtop);
 #pragma unroll
-    for (int i = 0; i < kChunkPerThread; ++i)
-        if (t0 + i * kChunkThreads + tid < V) s += exp((double)zv[i] - m);
-    s = block_sum_f64(s, s_red);  // its barriers also publish s_top
-    if (tid < k) out[tid] = s_top[tid];
-    if (tid == 0) {
-        cmax[row * C + c] = (float)m;
-        csum[row * C + c] = s;
+        for (int i = 0; i < kChunkPerLane; ++i)
+            if (t0 + i * kWave + lane < V) s += exp((double)zv[i] - wm);
+    }
+    s = wave_sum_f64(s);
+    if (lane < k) s_wl[wid][lane] = mine;
+    if (lane == 0) s_ws[wid] = s;
+    __syncthreads();
+    if (wid != 0) return;
+    // merge the four sorted wave lists by rank: a key's place in the chunk's list
+    // is the number of larger keys in the pool (keys are unique); lane l holds pool
+    // entries l and l + 64
+    const int pool = kChunkWaves * k;  // <= 128
+    const uint64_t c0 = lane < pool ? s_wl[lane / k][lane % k] : 0;
+    const uint64_t c1 = lane + kWave < pool ? s_wl[(lane + kWave) / k][(lane + kWave) % k] : 0;
+    int r0 = 0, r1 = 0, nz = 0;
+    for (int w = 0; w < kChunkWaves; ++w)
+        for (int i = 0; i < k; ++i) {
+            const uint64_t x = s_wl[w][i];  // the same entry in every lane
+            r0 += x > c0;
+            r1 += x > c1;
+            nz += x != 0;
+        }
+    uint64_t* out = ckeys + (row * C + c) * (size_t)k;
+    if (c0 != 0 && r0 < k) out[r0] = c0;
+    if (c1 != 0 && r1 < k) out[r1] = c1;
+    if (lane >= nz && lane < k) out[lane] = 0;  // fewer than k tokens in the chunk
+    // chunk max = the top key's logit; chunk sum = sum over waves of
+    // (wave sum) * exp(wave max - chunk max), all in fp64
+    uint64_t top = s_wl[0][0];
+#pragma unroll
+    for (int w = 1; w < kChunkWaves; ++w) top = s_wl[w][0] > top ? s_wl[w][0] : top;
+    double part = 0.0;
+    if (lane < kChunkWaves && top != 0) {
+        const uint64_t wk = s_wl[lane][0];
+        if (wk != 0) part = s_ws[lane] * exp((double)logit_key_value(wk) - (double)logit_key_value(top));
+    }
+    part = wave_sum_f64(part);
+    if (lane == 0) {
+        cmax[row * C + c] = top != 0 ? logit_key_value(top) : 0.0f;
+        csum[row * C + c] = part;
     }
 }
 
@@ -90,6 +119,69 @@ __global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
 constexpr int kFinishThreads = 1024;
 constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kMergeLdsKeys = 8192;  // 64 KB of chunk lists per pass
+constexpr int kMaxChunkHeads = 4;    // chunk lists per lane: C <= 256
+constexpr int kFrontierRounds = 32;  // up to this many frontier nodes: one wave selects them
+static_assert((EAGLE_MAX_VOCAB + kChunk - 1) / kChunk <= kMaxChunkHeads * kWave, "chunk lists per lane");
+static_assert(((EAGLE_MAX_VOCAB + kChunk - 1) / kChunk) * EAGLE_MAX_TOPK <= kMergeLdsKeys, "one row's lists fit");
+
+// A draft row's top-k by k rounds of a wave maximum over the heads of its sorted
+// chunk lists in LDS; lane q owns chunks q, q + 64, ... (NH of them).  Lane r ends
+// holding the r-th key.
+template <int NH>
+__device__ __forceinline__ uint64_t merge_chunk_lists(const uint64_t* lists, int C, int k, int lane) {
+    int pos[NH];
+    uint64_t h[NH];
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+        pos[u] = 0;
+        h[u] = lane + u * kWave < C ? lists[(lane + u * kWave) * k] : 0;
+    }
+    uint64_t mykey = 0;
+    for (int r = 0; r < k; ++r) {
+        uint64_t loc = h[0];
+#pragma unroll
+        for (int u = 1; u < NH; ++u) loc = h[u] > loc ? h[u] : loc;
+        const uint64_t best = wave_max_key_u64(loc);
+#pragma unroll
+        for (int u = 0; u < NH; ++u)
+            if (best != 0 && h[u] == best) {  // keys are unique: one owner, which moves to its next key
+                ++pos[u];
+                h[u] = pos[u] < k ? lists[(lane + u * kWave) * k + pos[u]] : 0;
+            }
+        if (lane == r) mykey = best;
+    }
+    return mykey;
+}
+
+// The first `keep` of L candidate keys (held NQ per lane, lane + 64 q) by that many
+// rounds of a wave maximum; lane r ends holding the r-th.
+template <int NQ>
+__device__ __forceinline__ uint64_t select_top(uint64_t (&cand)[NQ], int keep, int lane) {
+    uint64_t pick = 0;
+    for (int r = 0; r < keep; ++r) {
+        uint64_t loc = cand[0];
+#pragma unroll
+        for (int q = 1; q < NQ; ++q) loc = cand[q] > loc ? cand[q] : loc;
+        const uint64_t best = wave_max_key_u64(loc);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            if (cand[q] == best) cand[q] = 0;  // keys are unique: one owner
+        if (lane == r) pick = best;
+    }
+    return pick;
+}
+
+template <int NQ>
+__device__ __forceinline__ uint64_t frontier_pick(const float* s_val, int L, int base, int keep, int lane) {
+    uint64_t cand[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int i = lane + q * kWave;
+        cand[q] = i < L ? ((uint64_t)float_order_key(s_val[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(base + i))
+                        : 0;
+    }
+    return select_top<NQ>(cand, keep, lane);
+}
 
 __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
     int rows, int k, int C, int layer, int depth_total, const uint64_t* __restrict__ ckeys,
@@ -119,34 +211,38 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
         const bool active = wid < waves && j < rows;
         uint64_t* mine = lists + wid * per_row;
         const size_t row = (size_t)b * rows + j;
-        if (active)
+        // everything this row needs from memory is requested before the merge:
+        // its chunk lists, chunk maxima and sums, its frontier node and that node's value
+        double cs[kMaxChunkHeads];
+        float cm[kMaxChunkHeads];
+        int f = 0;
+        float fval = 0.0f;
+        if (active) {
             for (int i = lane; i < per_row; i += kWave) mine[i] = ckeys[row * per_row + i];
+#pragma unroll
+            for (int u = 0; u < kMaxChunkHeads; ++u) {
+                const int cu = lane + u * kWave;
+                cs[u] = cu < C ? csum[row * C + cu] : 0.0;
+                cm[u] = cu < C ? cmax[row * C + cu] : 0.0f;
+            }
+            if (layer != 1) {
+                f = frontier[(size_t)b * m + j];
+                fval = value[(size_t)b * cap + f];
+            }
+        }
         __syncthreads();
         if (active) {
-            // lane q owns chunks q and q + 64 (C <= 128)
-            int p0 = 0, p1 = 0;
-            uint64_t mykey = 0;
-            for (int r = 0; r < k; ++r) {
-                const uint64_t h0 = (lane < C && p0 < k) ? mine[lane * k + p0] : 0;
-                const uint64_t h1 = (lane + kWave < C && p1 < k) ? mine[(lane + kWave) * k + p1] : 0;
-                const uint64_t loc = h0 > h1 ? h0 : h1;
-                const uint64_t best = wave_max_u64(loc);
-                if (best != 0) {
-                    if (h0 == best) ++p0;
-                    else if (h1 == best) ++p1;
-                }
-                if (lane == r) mykey = best;
-            }
+            const uint64_t mykey = C <= kWave       ? merge_chunk_lists<1>(mine, C, k, lane)
+                                   : C <= 2 * kWave ? merge_chunk_lists<2>(mine, C, k, lane)
+                                                    : merge_chunk_lists<4>(mine, C, k, lane);
             const uint64_t top = __shfl(mykey, 0, kWave);
             const float row_max = logit_key_value(top);
             double s = 0.0;
-            if (lane < C) s += csum[row * C + lane] * exp((double)cmax[row * C + lane] - (double)row_max);
-            if (lane + kWave < C)
-                s += csum[row * C + lane + kWave] * exp((double)cmax[row * C + lane + kWave] - (double)row_max);
+#pragma unroll
+            for (int u = 0; u < kMaxChunkHeads; ++u)
+                if (lane + u * kWave < C) s += cs[u] * exp((double)cm[u] - (double)row_max);
             s = wave_sum_f64(s);
             const float lse32 = (float)log(s);
-            const int f = (layer == 1) ? 0 : frontier[(size_t)b * m + j];
-            const float fval = (layer == 1) ? 0.0f : value[(size_t)b * cap + f];
             if (lane < k) {
                 const uint32_t tok = logit_key_token(mykey);
                 const float shifted = logit_key_value(mykey) - row_max;  // fp32
@@ -162,7 +258,16 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
         }
         __syncthreads();  // the lists area is reused by the next pass; every frontier entry read
     }
-    if (layer < depth_total) {
+    if (layer < depth_total && (L < m ? L : m) <= kFrontierRounds) {
+        // frontier = the first min(m, L) new nodes in (value desc, id asc): by that
+        // many rounds of a wave maximum over the layer
+        if (wid == 0) {
+            const int keep = L < m ? L : m;
+            const uint64_t pick = L <= 2 * kWave ? frontier_pick<2>(s_val, L, base, keep, lane)
+                                                 : frontier_pick<EAGLE_MAX_LAYER_NODES / kWave>(s_val, L, base, keep, lane);
+            if (lane < keep) frontier[(size_t)b * m + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(pick & 0xFFFFFFFFu));
+        }
+    } else if (layer < depth_total) {
         const int P = next_pow2(L);
         for (int i = tid; i < P; i += kFinishThreads) {
             uint64_t key = 0;
