@@ -395,11 +395,13 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     // the loader issues and waits for loads. ----
     Walker wf = w0;           // next tile to fetch
     int nl = 0;               // tiles fetched so far
-    int q_slot_tile = 0;      // tile whose Q is in (or on its way to) the Q slot
-    // The first segment's Q goes through the slot, issued ahead of the first tiles.
-    if (loader) load_q(a, w0.unit, qslot, mslot, wid - kComputeWaves, lane);
-    // A later segment's Q rides with its first tile into the slot when the slot is
-    // free; otherwise that tile loads its Q directly when its scores are computed.
+    int q_slot_tile = -1;     // tile whose Q is in (or on its way to) the Q slot
+    // The computing waves load the first segment's Q straight into registers: they
+    // have nothing else in flight, and it lands while tile 0's K streams in.  That
+    // keeps the slot free from the start for the next segment's Q, which rides with
+    // that segment's first tile (a third segment starting while the slot is still
+    // busy loads its Q directly when its scores are computed).
+    if (!loader) load_q_direct(w0.unit);
     auto fetch = [&]() {
         const Tile t = peek(wf, x_begin, x_end, S);
         if (loader) load_tile(a, t, row0, smem + (nl % kStages) * kStageBytes, off4, wid - kComputeWaves, lane);
@@ -412,19 +414,15 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     };
     fetch();
     if (wf.x < x_end) fetch();
-    // the Q slot and tile 0's K; its V and tile 1 may still be in flight, since the
-    // first iteration's barrier waits for both.  A one-tile stretch has no such
-    // barrier: there everything must land here.
+    // tile 0's K; its V and tile 1 (with any Q that rode with it) may still be in
+    // flight, since the first iteration's barrier waits for them.  A one-tile
+    // stretch has no such barrier: there everything must land here.
     if (loader) {
         if (nl > 1) vm_wait<kTileLoads / 2 + kTileLoads>();
         else vm_wait<0>();
     }
     barrier_lds();
     if (wf.x < x_end) fetch();        // tile 2: its stage has not been used yet
-    if (!loader) {
-        read_q_slot();
-    }
-    q_slot_tile = -1;  // free once every wave has passed the next barrier
 
     const int krow = 32 * ks + key_of_row(l32);
     const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
