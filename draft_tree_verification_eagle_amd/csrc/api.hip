@@ -111,7 +111,8 @@ static int attn_desc_check(const eagle_attn_desc* d) {
         return EAGLE_ERR_INVALID_ARG;
     if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
     if (d->T > EAGLE_MAX_TREE_ROWS) return EAGLE_ERR_UNSUPPORTED;
-    if (d->dtype == EAGLE_BF16 && (d->head_dim != 128 || d->batch > attention_max_batch()))
+    if (d->dtype == EAGLE_BF16 &&
+        (d->head_dim != 128 || d->batch > attention_max_batch() || !eagle::attention_split_fits(*d)))
         return EAGLE_ERR_UNSUPPORTED;
     if (d->dtype == EAGLE_F32 && d->head_dim > 128) return EAGLE_ERR_UNSUPPORTED;
     return EAGLE_OK;

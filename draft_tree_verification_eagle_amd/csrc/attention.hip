@@ -200,38 +200,50 @@ struct AttnArgs {
 // stretch is at least one tile plus one segment long, so each one holds a tile,
 // and the workgroups holding a unit's tiles are consecutive.
 constexpr int kSegCost4 = 2;
+// All in 32-bit steps: the host checks that the cost line fits in 31 bits.
 struct Split {
-    int64_t W;      // cost steps per unit
-    int64_t Wt;     // cost steps in all
-    int nt;         // tiles per unit
-    int nwg;        // workgroups that take part
+    uint32_t W;      // cost steps per unit
+    uint32_t Wt;     // cost steps in all
+    uint32_t q, r;   // Wt = q * nwg + r
+    int nt;          // tiles per unit
+    int nwg;         // workgroups that take part
 };
 __device__ __forceinline__ Split make_split(int S, int units, int grid) {
     Split sp;
     sp.nt = (S + kTileKeys - 1) / kTileKeys;
-    sp.W = 4 * (int64_t)sp.nt + kSegCost4;
-    sp.Wt = (int64_t)units * sp.W;
-    const int64_t most = sp.Wt / (4 + kSegCost4);
-    sp.nwg = most < (int64_t)grid ? (most > 0 ? (int)most : 1) : grid;
+    sp.W = 4u * (uint32_t)sp.nt + kSegCost4;
+    sp.Wt = (uint32_t)units * sp.W;
+    const uint32_t most = sp.Wt / (4 + kSegCost4);
+    sp.nwg = most < (uint32_t)grid ? (most > 0 ? (int)most : 1) : grid;
+    sp.q = sp.Wt / (uint32_t)sp.nwg;
+    sp.r = sp.Wt - sp.q * (uint32_t)sp.nwg;
     return sp;
 }
-// Key-list position (unit * S + key) of the first tile starting at or after cost
-// step p; units * S past the last tile.
-__device__ __forceinline__ int64_t split_key(const Split& sp, int S, int64_t p) {
-    int64_t u = p / sp.W;
-    const int64_t r = p - u * sp.W;
-    int64_t t = r <= kSegCost4 ? 0 : (r - kSegCost4 + 3) / 4;
-    if (t >= sp.nt) {
-        ++u;
-        t = 0;
-    }
-    return u * S + t * kTileKeys;
+// First cost step of stretch v: floor(Wt * v / nwg).
+__device__ __forceinline__ uint32_t stretch_start(const Split& sp, int v) {
+    return sp.q * (uint32_t)v + (sp.r * (uint32_t)v) / (uint32_t)sp.nwg;
 }
-// Workgroup (in list order) whose stretch [Wt*v/n, Wt*(v+1)/n) holds cost step p.
-__device__ __forceinline__ int stretch_of(int64_t p, int64_t total, int nwg) {
-    int v = (int)((p * nwg) / total);
-    while (v + 1 < nwg && total * (v + 1) / nwg <= p) ++v;
-    while (v > 0 && total * v / nwg > p) --v;
+// First tile (unit, tile) starting at or after cost step p; (units, 0) past the last.
+struct TilePos {
+    int unit, tile;
+};
+__device__ __forceinline__ TilePos split_tile(const Split& sp, uint32_t p) {
+    TilePos tp;
+    tp.unit = (int)(p / sp.W);
+    const uint32_t r = p - (uint32_t)tp.unit * sp.W;
+    tp.tile = r <= kSegCost4 ? 0 : (int)((r - kSegCost4 + 3) / 4);
+    if (tp.tile >= sp.nt) {
+        ++tp.unit;
+        tp.tile = 0;
+    }
+    return tp;
+}
+// Workgroup (in list order) whose stretch holds cost step p.
+__device__ __forceinline__ int stretch_of(const Split& sp, uint32_t p) {
+    int v = (int)((double)p * (double)sp.nwg / (double)sp.Wt);
+    if (v > sp.nwg - 1) v = sp.nwg - 1;
+    while (v + 1 < sp.nwg && stretch_start(sp, v + 1) <= p) ++v;
+    while (v > 0 && stretch_start(sp, v) > p) --v;
     return v;
 }
 
@@ -348,7 +360,7 @@ template <bool kLoader>
 __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem, unsigned char* qslot,
                                           uint32_t* mslot, float (*s_ml)[2][2][kWave], int wid, int lane,
                                           int T, int ctx, int S, int64_t row0, int vwg, int64_t x_begin,
-                                          int64_t x_end) {
+                                          int64_t x_end, TilePos tb) {
     constexpr bool loader = kLoader;
     const int rb = wid & 1, ks = (wid >> 1) & 1;
     const int l32 = lane & 31, h2 = lane >> 5;
@@ -362,8 +374,8 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
 
     Walker w0;
     w0.x = x_begin;
-    w0.unit = (int)(x_begin / S);
-    w0.key0 = (int)(x_begin - (int64_t)w0.unit * S);
+    w0.unit = tb.unit;
+    w0.key0 = tb.tile * kTileKeys;
 
     // ---- first segment's Q and mask word, straight into registers ----
     const int qrow = 32 * rb + l32;  // this lane's packed query row inside the unit
@@ -735,32 +747,36 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const Split sp = make_split(S, units, (int)gridDim.x);
     const int vwg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     if (vwg >= sp.nwg) return;
-    const int64_t x_begin = split_key(sp, S, sp.Wt * vwg / sp.nwg);
-    const int64_t x_end = split_key(sp, S, sp.Wt * (vwg + 1) / sp.nwg);
+    const TilePos tb = split_tile(sp, stretch_start(sp, vwg));
+    const TilePos te = split_tile(sp, stretch_start(sp, vwg + 1));
+    const int64_t x_begin = (int64_t)tb.unit * S + tb.tile * kTileKeys;
+    const int64_t x_end = (int64_t)te.unit * S + te.tile * kTileKeys;
     if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
 
     // waves 0..3 compute (query half, key half); wave 4 issues every K, V and Q
     // load and waits for them, so no computing wave stalls on a load issue.  Both
     // roles run the same tile walk and the same barriers.
     if (wid >= kComputeWaves)
-        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end);
+        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end, tb);
     else
-        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end);
+        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end, tb);
 
 }
 
 // ---------------------------------------------------------------------------
 // Merge: one workgroup per (unit, 16 query rows); thread = (row, 8 dims).
-// Partials are combined four at a time, their loads issued together.
+// Partials are combined kMergeBatch at a time, their loads issued together.
 // ---------------------------------------------------------------------------
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg) {
     const int tid = threadIdx.x;
     const int unit = blockIdx.x;
     const int g = unit / a.RG, rg = unit - g * a.RG;
     const int S = a.ctx_len[0] + a.T;
     const Split sp = make_split(S, a.Hkv * a.RG, grid_wg);
-    const int64_t p0 = (int64_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
-    const int vf = stretch_of(p0, sp.Wt, sp.nwg), vl = stretch_of(p0 + 4 * (int64_t)(sp.nt - 1), sp.Wt, sp.nwg);
+    const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
+    const int vf = stretch_of(sp, p0), vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
     if (vf == vl) return;  // written directly by the main kernel
     const int row = blockIdx.y * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
@@ -770,31 +786,34 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
     float acc[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) acc[x] = 0.0f;
-    for (int v0 = vf; v0 <= vl; v0 += 4) {
-        float mv[4], lv[4];
-        f16x8 ov[4];
+    // up to kMergeBatch partials per round, all requested together: slots past the
+    // last re-read the last one (same addresses) and get zero weight
+    for (int v0 = vf; v0 <= vl; v0 += kMergeBatch) {
+        float mv[kMergeBatch], lv[kMergeBatch];
+        f16x8 ov[kMergeBatch];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t slot = (int64_t)unit + v0 + j;
-            if (v0 + j <= vl) {
-                mv[j] = a.part_ml[slot * 128 + row];
-                lv[j] = a.part_ml[slot * 128 + 64 + row];
-                ov[j] = *(const f16x8*)(a.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
-            } else {
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const int64_t slot = (int64_t)unit + (v0 + j <= vl ? v0 + j : vl);
+            mv[j] = a.part_ml[slot * 128 + row];
+            lv[j] = a.part_ml[slot * 128 + 64 + row];
+            ov[j] = *(const f16x8*)(a.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+            if (v0 + j > vl) {
                 mv[j] = -INFINITY;
                 lv[j] = 0.0f;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) ov[j][x] = (_Float16)0.0f;
             }
-        }
-        const float Mn = fmaxf(fmaxf(M, fmaxf(mv[0], mv[1])), fmaxf(mv[2], mv[3]));
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, mv[j]);
         const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
         const float sc = __builtin_amdgcn_exp2f(M - Mu);
         L *= sc;
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] *= sc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kMergeBatch; ++j) {
             const float w = __builtin_amdgcn_exp2f(mv[j] - Mu) * lv[j];
             L += w;
 #pragma unroll
@@ -886,6 +905,14 @@ WsLayout ws_layout(const eagle_attn_desc& d) {
 }  // namespace
 
 size_t attention_workspace_bytes(const eagle_attn_desc& d) { return ws_layout(d).total; }
+
+bool attention_split_fits(const eagle_attn_desc& d) {
+    if (d.dtype != EAGLE_BF16) return true;
+    const int64_t G = d.n_q_heads / d.n_kv_heads;
+    const int64_t units = (int64_t)d.n_kv_heads * ((G * d.T + kUnitRows - 1) / kUnitRows);
+    const int64_t tiles = (d.kv_rows_total + kTileKeys - 1) / kTileKeys;  // bounds ctx + T of any sequence
+    return units * (4 * tiles + kSegCost4) < ((int64_t)1 << 31);
+}
 
 hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k, const void* v,
                             const uint64_t* mask, void* o, float* lse, void* workspace,

@@ -28,6 +28,9 @@ hipError_t launch_mask(const eagle_tree_cfg& cfg, int cap, const eagle_tree_stat
 // Tree attention.  Workspace layout and launch shape are decided here.
 int attention_max_batch();
 size_t attention_workspace_bytes(const eagle_attn_desc& d);
+// The bf16 path splits its work on a 31-bit cost line; false if this shape would
+// not fit it.
+bool attention_split_fits(const eagle_attn_desc& d);
 hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k,
                             const void* v, const uint64_t* mask, void* o, float* lse,
                             void* workspace, hipStream_t stream);
