@@ -247,26 +247,28 @@ __device__ __forceinline__ int stretch_of(const Split& sp, uint32_t p) {
     return v;
 }
 
-// Position in a workgroup's stretch of the unit-major key list: list position x,
-// unit and key inside the unit.  Advanced tile by tile without division.
+// Position in a workgroup's stretch: keys walked since the stretch start (a
+// stretch is far below 2^31 keys), unit and key inside the unit.  Advanced tile by
+// tile without division; all bookkeeping is 32-bit scalar work.
 struct Walker {
-    int64_t x;
+    int x;
     int unit, key0;
 };
 struct Tile {
     int unit, key0, nkeys;
     bool seg_start, seg_end;
 };
-__device__ __forceinline__ Tile peek(const Walker& w, int64_t x_begin, int64_t x_end, int S) {
+// `len` = keys in the stretch.
+__device__ __forceinline__ Tile peek(const Walker& w, int len, int S) {
     Tile t;
     t.unit = w.unit;
     t.key0 = w.key0;
     int n = kTileKeys;
     if (S - w.key0 < n) n = S - w.key0;
-    if (x_end - w.x < n) n = (int)(x_end - w.x);
+    if (len - w.x < n) n = len - w.x;
     t.nkeys = n;
-    t.seg_start = (w.x == x_begin) || (w.key0 == 0);
-    t.seg_end = (w.x + n == x_end) || (w.key0 + n == S);
+    t.seg_start = (w.x == 0) || (w.key0 == 0);
+    t.seg_end = (w.x + n == len) || (w.key0 + n == S);
     return t;
 }
 __device__ __forceinline__ void advance(Walker& w, int nkeys, int S) {
@@ -359,8 +361,8 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int unit, unsigned cha
 template <bool kLoader>
 __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem, unsigned char* qslot,
                                           uint32_t* mslot, float (*s_ml)[2][2][kWave], int wid, int lane,
-                                          int T, int ctx, int S, int64_t row0, int vwg, int64_t x_begin,
-                                          int64_t x_end, TilePos tb) {
+                                          int T, int ctx, int S, int64_t row0, int vwg, int len,
+                                          TilePos tb) {
     constexpr bool loader = kLoader;
     const int rb = wid & 1, ks = (wid >> 1) & 1;
     const int l32 = lane & 31, h2 = lane >> 5;
@@ -373,7 +375,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
         off4[j] = (uint32_t)((lane >> 4) * kRowBytes + (((lane & 15) ^ swz(j * 4 + (lane >> 4))) << 4));
 
     Walker w0;
-    w0.x = x_begin;
+    w0.x = 0;
     w0.unit = tb.unit;
     w0.key0 = tb.tile * kTileKeys;
 
@@ -415,7 +417,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     // busy loads its Q directly when its scores are computed).
     if (!loader) load_q_direct(w0.unit);
     auto fetch = [&]() {
-        const Tile t = peek(wf, x_begin, x_end, S);
+        const Tile t = peek(wf, len, S);
         if (loader) load_tile(a, t, row0, smem + (nl % kStages) * kStageBytes, off4, wid - kComputeWaves, lane);
         if (t.seg_start && nl > 0 && q_slot_tile < 0) {
             if (loader) load_q(a, t.unit, qslot, mslot, wid - kComputeWaves, lane);
@@ -425,7 +427,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
         ++nl;
     };
     fetch();
-    if (wf.x < x_end) fetch();
+    if (wf.x < len) fetch();
     // tile 0's K; its V and tile 1 (with any Q that rode with it) may still be in
     // flight, since the first iteration's barrier waits for them.  A one-tile
     // stretch has no such barrier: there everything must land here.
@@ -434,7 +436,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
         else vm_wait<0>();
     }
     barrier_lds();
-    if (wf.x < x_end) fetch();        // tile 2: its stage has not been used yet
+    if (wf.x < len) fetch();        // tile 2: its stage has not been used yet
 
     const int krow = 32 * ks + key_of_row(l32);
     const int g16 = lane >> 4, i16 = lane & 15, rr = i16 >> 2, cc = i16 & 3, dh = g16 & 1;
@@ -455,7 +457,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
 
     // ---- tile 0: scores ----
     Walker wn = w0;           // tile whose scores are computed next
-    Tile tc = peek(wn, x_begin, x_end, S);
+    Tile tc = peek(wn, len, S);
     advance(wn, tc.nkeys, S);
     f32x16 sacc;
     if (!loader) sacc = scores(smem);
@@ -472,15 +474,15 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     // Software pipeline: iteration it computes the scores of tile it+1 (MFMA)
     // next to the softmax of tile it (VALU), then PV of tile it.
     for (int it = 0;; ++it) {
-        const bool has_next = wn.x < x_end;
+        const bool has_next = wn.x < len;
         Tile tn;
         bool from0_n = from0_c;
         if (has_next) {
             // tile it+1 has landed; tile it-1's stage is free
             if (loader) loader_wait(nl - it - 2);
             barrier_lds();
-            if (wf.x < x_end) fetch();
-            tn = peek(wn, x_begin, x_end, S);
+            if (wf.x < len) fetch();
+            tn = peek(wn, len, S);
             if (tn.seg_start) {
                 if (q_slot_tile == it + 1) {
                     if (!loader) {
@@ -752,14 +754,15 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const int64_t x_begin = (int64_t)tb.unit * S + tb.tile * kTileKeys;
     const int64_t x_end = (int64_t)te.unit * S + te.tile * kTileKeys;
     if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
+    const int len = (int)(x_end - x_begin);
 
     // waves 0..3 compute (query half, key half); wave 4 issues every K, V and Q
     // load and waits for them, so no computing wave stalls on a load issue.  Both
     // roles run the same tile walk and the same barriers.
     if (wid >= kComputeWaves)
-        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end, tb);
+        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, len, tb);
     else
-        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, x_begin, x_end, tb);
+        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, len, tb);
 
 }
 
