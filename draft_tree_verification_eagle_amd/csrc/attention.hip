@@ -199,7 +199,7 @@ struct AttnArgs {
 // boundaries and a workgroup that spans two units takes fewer tiles.  Every
 // stretch is at least one tile plus one segment long, so each one holds a tile,
 // and the workgroups holding a unit's tiles are consecutive.
-constexpr int kSegCost4 = 2;
+constexpr int kSegCost4 = 6;
 // All in 32-bit steps: the host checks that the cost line fits in 31 bits.
 struct Split {
     uint32_t W;      // cost steps per unit

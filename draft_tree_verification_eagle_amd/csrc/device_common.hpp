@@ -103,6 +103,32 @@ __device__ __forceinline__ uint64_t wave_max_key_u64(uint64_t v) {
     return ((uint64_t)mhi << 32) | mlo;
 }
 
+// e^x for x <= 0 in fp64, within about 1 ulp of the correctly rounded value (0 for
+// x < -745).  Cody and Waite's reduction x = n ln2 + r, ln2 split in two parts (the
+// first with 21 trailing zero bits, so n * hi is exact), |r| <= ln2 / 2; then the
+// degree-13 Taylor polynomial of e^r (truncation error below 2e-17) by Horner, and
+// the scale by 2^n.
+__device__ __forceinline__ double exp_nonpos_f64(double x) {
+    if (x < -745.0) return 0.0;
+    const double n = __builtin_rint(x * 1.4426950408889634);
+    const double r = __builtin_fma(-n, 1.90821492927058770002e-10, __builtin_fma(-n, 6.93147180369123816490e-01, x));
+    double p = 1.0 / 6227020800.0;         // 1/13!
+    p = __builtin_fma(p, r, 1.0 / 479001600.0);  // 1/12!
+    p = __builtin_fma(p, r, 1.0 / 39916800.0);
+    p = __builtin_fma(p, r, 1.0 / 3628800.0);
+    p = __builtin_fma(p, r, 1.0 / 362880.0);
+    p = __builtin_fma(p, r, 1.0 / 40320.0);
+    p = __builtin_fma(p, r, 1.0 / 5040.0);
+    p = __builtin_fma(p, r, 1.0 / 720.0);
+    p = __builtin_fma(p, r, 1.0 / 120.0);
+    p = __builtin_fma(p, r, 1.0 / 24.0);
+    p = __builtin_fma(p, r, 1.0 / 6.0);
+    p = __builtin_fma(p, r, 0.5);
+    p = __builtin_fma(p, r, 1.0);
+    p = __builtin_fma(p, r, 1.0);
+    return __builtin_ldexp(p, (int)n);
+}
+
 __device__ __forceinline__ double u64_f64(uint64_t u) { return __longlong_as_double((long long)u); }
 __device__ __forceinline__ uint64_t f64_u64(double d) { return (uint64_t)__double_as_longlong(d); }
 

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
                     const int t = (it0 + q) * kRowThreads + tid;
                     if (t < V && !((kb >> q) & 1u)) {
                         const double x = (double)zr[q] - (double)zmax;
-                        s += exp(unit_temp ? x : x / temp);
+                        s += exp_nonpos_f64(unit_temp ? x : x / temp);
                     }
                 }
             }
@@ -131,11 +131,11 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
             for (int t = tid; t < V; t += kRowThreads) {
                 bool kid = false;
                 for (int c = 0; c < nk; ++c) kid |= (s_kid_tok[c] == t);
-                if (!kid) s += exp(((double)z[t] - (double)zmax) / temp);
+                if (!kid) s += exp_nonpos_f64(((double)z[t] - (double)zmax) / temp);
             }
         }
         s = block_sum_f64(s, s_red);
-        if (tid < nk) out->kid_e[tid] = exp(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
+        if (tid < nk) out->kid_e[tid] = exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
         if (tid == 0) out->rest = s;
     }
     if (tid < nk) out->kid_row[tid] = s_kid_row[tid];
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                 mass[q] = 0;
                 if (t0 + q < t1 && !((rm >> q) & 1u)) {
                     const double x = (double)z[t0 + q] - zmax;
-                    mass[q] = fixed_mass(exp(unit_temp ? x : x / temp));
+                    mass[q] = fixed_mass(exp_nonpos_f64(unit_temp ? x : x / temp));
                 }
                 cs += mass[q];
             }
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                 for (int q = 0; q < 64 && a0 + q < t1; ++q)
                     if (!((rm[w] >> q) & 1ull)) {
                         const double x = (double)z[a0 + q] - zmax;
-                        cs += fixed_mass(exp(unit_temp ? x : x / temp));
+                        cs += fixed_mass(exp_nonpos_f64(unit_temp ? x : x / temp));
                     }
             }
             const uint64_t prefix = block_exclusive_scan_u64(cs, s_wave, &total);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                     for (int q = 0; q < 64 && a0 + q < t1 && !done; ++q) {
                         if ((rm[w] >> q) & 1ull) continue;
                         const double x = (double)z[a0 + q] - zmax;
-                        run += fixed_mass(exp(unit_temp ? x : x / temp));
+                        run += fixed_mass(exp_nonpos_f64(unit_temp ? x : x / temp));
                         if (run > goal) {
                             s_out[s_len] = a0 + q;
                             done = true;
