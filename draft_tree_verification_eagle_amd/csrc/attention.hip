@@ -197,9 +197,11 @@ struct AttnArgs {
 // key-half merge and its output).  The line is cut into nwg equal stretches and a
 // workgroup takes the tiles that start in its stretch, so stretches end on tile
 // boundaries and a workgroup that spans two units takes fewer tiles.  Every
-// stretch is at least one tile plus one segment long, so each one holds a tile,
-// and the workgroups holding a unit's tiles are consecutive.
-constexpr int kSegCost4 = 6;
+// stretch is at least one tile long, so one that lies inside a unit's tiles holds
+// a tile start; one that falls wholly in the steps before a unit's first tile is
+// empty (its workgroup exits).  The workgroups holding a unit's tiles are
+// consecutive, none of them empty.
+constexpr int kSegCost4 = 16;
 // All in 32-bit steps: the host checks that the cost line fits in 31 bits.
 struct Split {
     uint32_t W;      // cost steps per unit
@@ -213,7 +215,7 @@ __device__ __forceinline__ Split make_split(int S, int units, int grid) {
     sp.nt = (S + kTileKeys - 1) / kTileKeys;
     sp.W = 4u * (uint32_t)sp.nt + kSegCost4;
     sp.Wt = (uint32_t)units * sp.W;
-    const uint32_t most = sp.Wt / (4 + kSegCost4);
+    const uint32_t most = sp.Wt / 4;
     sp.nwg = most < (uint32_t)grid ? (most > 0 ? (int)most : 1) : grid;
     sp.q = sp.Wt / (uint32_t)sp.nwg;
     sp.r = sp.Wt - sp.q * (uint32_t)sp.nwg;
@@ -753,7 +755,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const TilePos te = split_tile(sp, stretch_start(sp, vwg + 1));
     const int64_t x_begin = (int64_t)tb.unit * S + tb.tile * kTileKeys;
     const int64_t x_end = (int64_t)te.unit * S + te.tile * kTileKeys;
-    if (x_begin >= x_end) return;  // cannot happen: every stretch holds a tile
+    if (x_begin >= x_end) return;  // a stretch in the steps before a unit's first tile
     const int len = (int)(x_end - x_begin);
 
     // waves 0..3 compute (query half, key half); wave 4 issues every K, V and Q

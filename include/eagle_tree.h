@@ -151,7 +151,7 @@ int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
  * host; the call checks kv_rows_total >= batch * T).
  * Supported: BF16 with head_dim 128; F32 with head_dim <= 128; T <= 64;
  * batch <= EAGLE_MAX_BATCH; for BF16 also
- *     n_kv_heads * ceil(G * T / 64) * (4 * ceil(kv_rows_total / 64) + 6) < 2^31,
+ *     n_kv_heads * ceil(G * T / 64) * (4 * ceil(kv_rows_total / 64) + 16) < 2^31,
  * G = n_q_heads / n_kv_heads (otherwise EAGLE_ERR_UNSUPPORTED).  BF16 runs one
  * sequence per kernel launch pair.
  * The workspace (eagle_tree_attention_workspace bytes, none for F32) holds

@@ -154,9 +154,9 @@ def test_attention_validation(eb):
     assert call(_desc(eb, scale=float("nan"))) == eb.EAGLE_ERR_INVALID_ARG
     assert call(_desc(eb, rows=60)) == eb.EAGLE_ERR_INVALID_ARG             # rows < batch * T
     assert call(_desc(eb, batch=1025, rows=10 ** 6)) == eb.EAGLE_ERR_UNSUPPORTED
-    # bf16 work split: units * (4 * ceil(rows / 64) + 6) must stay below 2^31
-    # (40 units: rows up to 64 * (2^31 / 40 - 6) / 4 fit)
-    limit_tiles = ((1 << 31) // 40 - 6) // 4
+    # bf16 work split: units * (4 * ceil(rows / 64) + 16) must stay below 2^31
+    # (40 units: rows up to 64 * (2^31 / 40 - 16) / 4 fit)
+    limit_tiles = ((1 << 31) // 40 - 16) // 4
     assert L.eagle_tree_attention_workspace(C.byref(_desc(eb, rows=64 * limit_tiles))) > 0
     assert L.eagle_tree_attention_workspace(C.byref(_desc(eb, rows=64 * limit_tiles + 64))) == 0
     assert call(_desc(eb, rows=64 * limit_tiles + 64)) == eb.EAGLE_ERR_UNSUPPORTED
