@@ -13,8 +13,8 @@
 //    CU, on tile boundaries and weighted so that a workgroup spanning two units
 //    (two segments to merge and write) takes fewer tiles.  Workgroup index ->
 //    list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD takes one
-//    contiguous stretch, so the units that share K/V rows (GQA) read them
-//    through one L2.
+//    contiguous run of stretches, so the units that share K/V rows (GQA) read
+//    them through one L2, and the partials of a unit land mostly in one L2.
 //  * Eight waves per workgroup: four compute, four only load.  K and V stream HBM ->
 //    LDS by direct 16-byte global_load_lds (no register staging), four stages
 //    deep, issued and waited for by the loader waves alone (each issues a quarter
@@ -43,7 +43,9 @@
 //    it writes a partial: row max and row sum in fp32 and the normalised row in
 //    fp16 (relative rounding 2^-11, inside the bf16 output's own).  The merge
 //    kernel, on the same stream, combines the partials of split units, so no
-//    workgroup ever waits for another.
+//    workgroup ever waits for another; each unit is merged on the XCD whose
+//    stretches hold the middle of it, where most of its partials are still in
+//    L2 (written back, not dropped, when the main kernel ends).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -73,6 +75,19 @@ constexpr int kLoaders = EAGLE_LOADERS;              // waves that issue the loa
 constexpr int kThreads = (kComputeWaves + kLoaders) * 64;
 constexpr int kStages = 4;
 constexpr int kGridWG = 256;                         // one per CU, multiple of the 8 XCDs
+static_assert(kGridWG % 8 == 0, "workgroups are dealt to the 8 XCDs in turn");
+
+// Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
+// the XCDs in turn).  Of n stretches, XCD x takes [xcd_first(x, n),
+// xcd_first(x + 1, n)): one contiguous run each, sizes differing by at most one.
+__host__ __device__ inline int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
+// Unit u's middle lies at fraction (u + 1/2) / units of the cost line, which
+// XCD floor((8u + 4) / units) holds; XCD x merges units [merge_unit_first(x),
+// merge_unit_first(x + 1)), at most ceil(units / 8) of them.
+__host__ __device__ inline int merge_unit_first(int x, int units) {
+    const int t = x * units - 4;
+    return t <= 0 ? 0 : (t + 7) >> 3;
+}
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kTileKeys * kRowBytes;    // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;          // K tile | V tile
@@ -749,8 +764,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const int64_t row0 = a.kv_row_off[0];
     const int units = a.Hkv * a.RG;
     const Split sp = make_split(S, units, (int)gridDim.x);
-    const int vwg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    if (vwg >= sp.nwg) return;
+    const int xcd = blockIdx.x & 7;
+    const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
+    if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
     const TilePos tb = split_tile(sp, stretch_start(sp, vwg));
     const TilePos te = split_tile(sp, stretch_start(sp, vwg + 1));
     const int64_t x_begin = (int64_t)tb.unit * S + tb.tile * kTileKeys;
@@ -771,19 +787,25 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 // ---------------------------------------------------------------------------
 // Merge: one workgroup per (unit, 16 query rows); thread = (row, 8 dims).
 // Partials are combined kMergeBatch at a time, their loads issued together.
+// Workgroup b: XCD x = b % 8, then the (b / 8)-th (unit, row block) of the units
+// XCD x merges; the grid holds 8 * ceil(units / 8) * kRowBlocks workgroups.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
+constexpr int kRowBlocks = kUnitRows / 16;
 
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg) {
     const int tid = threadIdx.x;
-    const int unit = blockIdx.x;
+    const int units = a.Hkv * a.RG;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int unit = merge_unit_first(xcd, units) + j / kRowBlocks;
+    if (unit >= merge_unit_first(xcd + 1, units)) return;
     const int g = unit / a.RG, rg = unit - g * a.RG;
     const int S = a.ctx_len[0] + a.T;
-    const Split sp = make_split(S, a.Hkv * a.RG, grid_wg);
+    const Split sp = make_split(S, units, grid_wg);
     const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
     const int vf = stretch_of(sp, p0), vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
     if (vf == vl) return;  // written directly by the main kernel
-    const int row = blockIdx.y * 16 + (tid >> 4);
+    const int row = (j % kRowBlocks) * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
     const int rp = rg * kUnitRows + row;
     if (rp >= a.G * a.T) return;
@@ -956,7 +978,8 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         tree_attn_bf16_kernel<<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + the loader
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        tree_attn_merge_kernel<<<dim3(d.n_kv_heads * RG, kUnitRows / 16), 256, 0, stream>>>(a, kGridWG);
+        const int merge_wg = 8 * ((d.n_kv_heads * RG + 7) / 8) * kRowBlocks;
+        tree_attn_merge_kernel<<<merge_wg, 256, 0, stream>>>(a, kGridWG);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
