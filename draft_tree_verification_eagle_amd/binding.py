@@ -10,6 +10,8 @@ import ctypes as C
 import os
 from dataclasses import dataclass
 
+import numpy as np
+
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeagle_tree.so")
 
 EAGLE_OK, EAGLE_ERR_INVALID_ARG, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_WORKSPACE, EAGLE_ERR_HIP = 0, -1, -2, -3, -4
@@ -36,7 +38,8 @@ class TreeStateC(C.Structure):
 class AttnDesc(C.Structure):
     _fields_ = [("dtype", C.c_int), ("batch", C.c_int32), ("T", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ctx_len", C.c_void_p),
-                ("kv_row_off", C.c_void_p), ("kv_rows_total", C.c_int64), ("scale", C.c_float)]
+                ("kv_row_off", C.c_void_p), ("kv_rows_total", C.c_int64), ("scale", C.c_float),
+                ("ctx_len_host", C.c_void_p), ("kv_row_off_host", C.c_void_p)]
 
 
 def load_library(path: str = _LIB_PATH) -> C.CDLL:
@@ -118,9 +121,22 @@ class TreeState:
 
 
 def make_attn_desc(dtype: int, batch: int, T: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
-                   ctx_len, kv_row_off, kv_rows_total: int, scale: float = 0.0) -> AttnDesc:
-    return AttnDesc(dtype, batch, T, n_q_heads, n_kv_heads, head_dim, _ptr(ctx_len), _ptr(kv_row_off),
-                    int(kv_rows_total), float(scale))
+                   ctx_len, kv_row_off, kv_rows_total: int, scale: float = 0.0,
+                   ctx_len_host=None, kv_row_off_host=None) -> AttnDesc:
+    """ctx_len / kv_row_off: device tensors.  ctx_len_host / kv_row_off_host: optional
+    host copies (array-likes, converted to contiguous int32 / int64 arrays that the
+    descriptor keeps alive)."""
+    hc = ho = None
+    if (ctx_len_host is None) != (kv_row_off_host is None):
+        raise ValueError("give both host copies or neither")
+    if ctx_len_host is not None:
+        hc = np.ascontiguousarray(ctx_len_host, dtype=np.int32)
+        ho = np.ascontiguousarray(kv_row_off_host, dtype=np.int64)
+    d = AttnDesc(dtype, batch, T, n_q_heads, n_kv_heads, head_dim, _ptr(ctx_len), _ptr(kv_row_off),
+                 int(kv_rows_total), float(scale),
+                 hc.ctypes.data if hc is not None else None, ho.ctypes.data if ho is not None else None)
+    d._host_copies = (hc, ho)
+    return d
 
 
 # ---------------------------------------------------------------------------

@@ -115,6 +115,13 @@ static int attn_desc_check(const eagle_attn_desc* d) {
         (d->head_dim != 128 || d->batch > attention_max_batch() || !eagle::attention_split_fits(*d)))
         return EAGLE_ERR_UNSUPPORTED;
     if (d->dtype == EAGLE_F32 && d->head_dim > 128) return EAGLE_ERR_UNSUPPORTED;
+    if ((d->ctx_len_host == nullptr) != (d->kv_row_off_host == nullptr)) return EAGLE_ERR_INVALID_ARG;
+    if (d->ctx_len_host) {
+        for (int b = 0; b < d->batch; ++b) {
+            const int64_t c = d->ctx_len_host[b], off = d->kv_row_off_host[b];
+            if (c < 0 || off < 0 || off > d->kv_rows_total - d->T - c) return EAGLE_ERR_INVALID_ARG;
+        }
+    }
     return EAGLE_OK;
 }
 

@@ -197,13 +197,15 @@ struct AttnArgs {
     const uint64_t* mask;      // [T]
     __bf16* o;                 // [T][Hq][D]
     float* lse;                // [T][Hq] or null
-    const int32_t* ctx_len;    // [1]
-    const int64_t* kv_row_off; // [1]
+    const int32_t* ctx_len;    // [1], read when ctx_h < 0
+    const int64_t* kv_row_off; // [1], read when ctx_h < 0
     _Float16* part_o;          // [slots][64][128], normalised rows
     float* part_ml;            // [slots][2][64]: row reference max (base 2), row sum
     int64_t kv_rows_total;
     int T, Hq, Hkv, G, RG;
     float scale_log2;
+    int ctx_h;                 // the sequence's context length from the host, or -1
+    int64_t row0_h;            // its first cache row from the host (when ctx_h >= 0)
 };
 
 // Work split.  Each unit's keys form nt = ceil(S / 64) tiles; the tiles are laid
@@ -759,9 +761,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int T = a.T;
-    const int ctx = a.ctx_len[0];
+    const bool host_len = a.ctx_h >= 0;  // uniform: a launch argument
+    const int ctx = host_len ? a.ctx_h : a.ctx_len[0];
     const int S = ctx + T;
-    const int64_t row0 = a.kv_row_off[0];
+    const int64_t row0 = host_len ? a.row0_h : a.kv_row_off[0];
     const int units = a.Hkv * a.RG;
     const Split sp = make_split(S, units, (int)gridDim.x);
     const int xcd = blockIdx.x & 7;
@@ -800,7 +803,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
     const int unit = merge_unit_first(xcd, units) + j / kRowBlocks;
     if (unit >= merge_unit_first(xcd + 1, units)) return;
     const int g = unit / a.RG, rg = unit - g * a.RG;
-    const int S = a.ctx_len[0] + a.T;
+    const int S = (a.ctx_h >= 0 ? a.ctx_h : a.ctx_len[0]) + a.T;
     const Split sp = make_split(S, units, grid_wg);
     const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
     const int vf = stretch_of(sp, p0), vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
@@ -975,6 +978,8 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.kv_rows_total = d.kv_rows_total;
         a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
         a.scale_log2 = scale * kLog2e;
+        a.ctx_h = d.ctx_len_host ? d.ctx_len_host[b] : -1;
+        a.row0_h = d.kv_row_off_host ? d.kv_row_off_host[b] : 0;
         tree_attn_bf16_kernel<<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + the loader
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

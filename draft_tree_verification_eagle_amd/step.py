@@ -20,7 +20,9 @@ from . import workload as wl
 class VerifyStep:
     def __init__(self, w: wl.Workload, device: str = "cuda", layers: Optional[int] = None,
                  draft: Optional[np.ndarray] = None, root: Optional[np.ndarray] = None,
-                 ctx_lens: Optional[np.ndarray] = None, with_lse: bool = True):
+                 ctx_lens: Optional[np.ndarray] = None, with_lse: bool = True, host_lengths: bool = True):
+        """host_lengths: also hand the attention call host copies of the context lengths
+        and cache row offsets (the library then passes them as launch arguments)."""
         self.w = w
         self.device = device
         B, T, V = w.batch, w.T, w.vocab
@@ -67,7 +69,9 @@ class VerifyStep:
         self.kv_row_off = torch.from_numpy(off).to(device)
         dtype = eb.EAGLE_F32 if w.dtype == "f32" else eb.EAGLE_BF16
         self.desc = eb.make_attn_desc(dtype, B, T, w.n_q_heads, w.n_kv_heads, w.head_dim, self.ctx_len,
-                                      self.kv_row_off, total)
+                                      self.kv_row_off, total,
+                                      ctx_len_host=lens if host_lengths else None,
+                                      kv_row_off_host=off if host_lengths else None)
         ws = eb.eagle_tree_attention_workspace(self.desc)
         self.attn_ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=device)
         # verification

@@ -156,7 +156,16 @@ int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
  * sequence per kernel launch pair.
  * The workspace (eagle_tree_attention_workspace bytes, none for F32) holds
  * split-KV partials; it needs no initialisation, and calls that share one must
- * be ordered on one stream. */
+ * be ordered on one stream.
+ * ctx_len_host / kv_row_off_host: optional host copies of ctx_len and kv_row_off
+ * (both or neither; NULL = the kernels read the device arrays).  When given they
+ * must hold the same values as the device arrays, and the BF16 kernels take each
+ * sequence's context length and first row as launch arguments instead of reading
+ * them when they start (one memory round trip less before the first load of each
+ * kernel).  The call checks 0 <= ctx_len_host[b], 0 <= kv_row_off_host[b] and
+ * kv_row_off_host[b] + ctx_len_host[b] + T <= kv_rows_total for every b
+ * (EAGLE_ERR_INVALID_ARG otherwise); the host copies are read during the call
+ * only.  F32 always reads the device arrays. */
 typedef struct {
     eagle_dtype dtype;
     int32_t batch, T, n_q_heads, n_kv_heads, head_dim;
@@ -164,6 +173,8 @@ typedef struct {
     const int64_t* kv_row_off; /* [batch] device */
     int64_t kv_rows_total;
     float scale; /* 0 => 1/sqrt(head_dim) */
+    const int32_t* ctx_len_host;    /* [batch] host, or NULL */
+    const int64_t* kv_row_off_host; /* [batch] host, or NULL */
 } eagle_attn_desc;
 
 size_t eagle_tree_attention_workspace(const eagle_attn_desc* desc);

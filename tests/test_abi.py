@@ -170,6 +170,29 @@ def test_attention_validation(eb):
     assert call(_desc(eb, batch=0, rows=0), None, 0) == eb.EAGLE_OK
 
 
+def test_attention_host_length_checks(eb):
+    """Host copies of ctx_len / kv_row_off: both or neither, and every sequence's
+    rows inside the cache (checked by the descriptor validation, seen here through
+    the workspace query, which returns 0 for a rejected descriptor)."""
+    L = eb.lib()
+    ws = lambda d: L.eagle_tree_attention_workspace(C.byref(d))
+    mk = lambda lens, offs, rows, batch=None: eb.make_attn_desc(
+        eb.EAGLE_BF16, len(lens) if batch is None else batch, 61, 40, 40, 128, None, None, rows,
+        ctx_len_host=lens, kv_row_off_host=offs)
+    assert ws(mk([4096], [0], 4157)) > 0
+    assert ws(mk([4096], [0], 4156)) == 0                     # last tree row past the cache
+    assert ws(mk([100, 200], [0, 161], 161 + 261)) > 0
+    assert ws(mk([100, 200], [0, 162], 161 + 261)) == 0
+    assert ws(mk([-1], [0], 4157)) == 0
+    assert ws(mk([10], [-1], 4157)) == 0
+    one = eb.make_attn_desc(eb.EAGLE_BF16, 1, 61, 40, 40, 128, None, None, 4157)
+    keep = mk([4096], [0], 4157)
+    one.ctx_len_host = keep.ctx_len_host                      # ctx_len_host without kv_row_off_host
+    assert ws(one) == 0
+    with pytest.raises(ValueError):
+        eb.make_attn_desc(eb.EAGLE_BF16, 1, 61, 40, 40, 128, None, None, 4157, ctx_len_host=[1])
+
+
 def test_attention_workspace_is_per_sequence_and_grows_with_units(eb):
     # partial slots are reused sequence after sequence, so the batch does not
     # change the size; more (KV head, row group) units need more slots

@@ -185,6 +185,23 @@ def test_attention_parity_tiny_f32_all_outputs(lib, orc):
     attention_check(orc, vs, trees, 0, None, atol=ATOL_F32)
 
 
+def same_without_host_lengths(eb, vs, layer=0):
+    """The call without host copies of the lengths (the kernels read the device
+    arrays) gives the same bits as the call with them."""
+    w = vs.w
+    dtype = eb.EAGLE_F32 if w.dtype == "f32" else eb.EAGLE_BF16
+    d = eb.make_attn_desc(dtype, w.batch, w.T, w.n_q_heads, w.n_kv_heads, w.head_dim, vs.ctx_len,
+                          vs.kv_row_off, vs.kv_rows_total)
+    a = vs.attn[layer]
+    o = torch.full_like(a["o"], float("nan"))
+    lse = None if a["lse"] is None else torch.full_like(a["lse"], float("nan"))
+    eb.eagle_tree_attention(d, a["q"], a["k"], a["v"], vs.mask, o, lse, vs.attn_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, a["o"])
+    if lse is not None:
+        assert torch.equal(lse, a["lse"])
+
+
 def test_attention_parity_7b_layer_all_outputs(lib, orc):
     eb, stepm, wl = lib
     w = wl.CONFIGS["llama2_7b_layer"]
@@ -195,6 +212,7 @@ def test_attention_parity_7b_layer_all_outputs(lib, orc):
     trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
     worst = attention_check(orc, vs, trees, 0, None)
     say(f"  worst |o - oracle| = {worst:.2e}")
+    same_without_host_lengths(eb, vs)
 
 
 def test_attention_parity_13b_sampled_layers(lib, orc):
@@ -303,6 +321,7 @@ def test_edge_cases(lib, orc, kw):
     dense_work = w.T * w.n_q_heads * (int(vs.ctx_lens_np.max()) + w.T) * w.batch
     attention_check(orc, vs, trees, 0, None if dense_work < 3e6 else 60,
                     atol=ATOL_F32 if w.dtype == "f32" else ATOL_BF16)
+    same_without_host_lengths(eb, vs)
     target, ft, fp = planted_target(wl, w, trees)
     verify_check(orc, vs, w, target, ft, fp, 0.0, 1, range(1))
     verify_check(orc, vs, w, target, ft, fp, 0.9, 31, range(6))
