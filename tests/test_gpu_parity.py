@@ -280,6 +280,23 @@ def test_verify_parity(lib, orc, name, temps):
         say(f"  exempt decisions {exempt}, mean accepted+1 = {tau:.2f}")
 
 
+@pytest.mark.parametrize("vocab", [131072, 100003])
+def test_verify_large_flat_vocabulary(lib, orc, vocab):
+    """Near-flat target rows over a large vocabulary at a high temperature: every mass
+    is close to 1, so a row's fixed-point total nears its 2^63 bound, and the bonus
+    chunks span 128 (vector loads) or 98 (scalar loads) tokens."""
+    eb, stepm, wl = lib
+    w = small(wl, vocab=vocab, target_sigma=0.001, n=7, depth=2, topk=4, m=2, ctx=20)
+    say(f"[verify parity] flat rows, vocab {vocab}, temperature 8")
+    vs = stepm.VerifyStep(w, layers=0)
+    vs.tree()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    target, ft, fp = planted_target(wl, w, trees)
+    exempt, tau = verify_check(orc, vs, w, target, ft, fp, 8.0, seed=99, steps=range(10))
+    say(f"  exempt decisions {exempt}, mean accepted+1 = {tau:.2f}")
+
+
 # ---------------------------------------------------------------------------
 # edge cases on small shapes
 # ---------------------------------------------------------------------------
