@@ -752,6 +752,9 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     }
 }
 
+// kHostLen: the sequence's context length and first row come as launch arguments
+// (a separate instantiation, so every argument load issues at once).
+template <bool kHostLen>
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
@@ -761,10 +764,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int T = a.T;
-    const bool host_len = a.ctx_h >= 0;  // uniform: a launch argument
-    const int ctx = host_len ? a.ctx_h : a.ctx_len[0];
+    const int ctx = kHostLen ? a.ctx_h : a.ctx_len[0];
     const int S = ctx + T;
-    const int64_t row0 = host_len ? a.row0_h : a.kv_row_off[0];
+    const int64_t row0 = kHostLen ? a.row0_h : a.kv_row_off[0];
     const int units = a.Hkv * a.RG;
     const Split sp = make_split(S, units, (int)gridDim.x);
     const int xcd = blockIdx.x & 7;
@@ -796,6 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 constexpr int kMergeBatch = 8;
 constexpr int kRowBlocks = kUnitRows / 16;
 
+template <bool kHostLen>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg) {
     const int tid = threadIdx.x;
     const int units = a.Hkv * a.RG;
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
     const int unit = merge_unit_first(xcd, units) + j / kRowBlocks;
     if (unit >= merge_unit_first(xcd + 1, units)) return;
     const int g = unit / a.RG, rg = unit - g * a.RG;
-    const int S = (a.ctx_h >= 0 ? a.ctx_h : a.ctx_len[0]) + a.T;
+    const int S = (kHostLen ? a.ctx_h : a.ctx_len[0]) + a.T;
     const Split sp = make_split(S, units, grid_wg);
     const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
     const int vf = stretch_of(sp, p0), vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
@@ -980,11 +983,17 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.scale_log2 = scale * kLog2e;
         a.ctx_h = d.ctx_len_host ? d.ctx_len_host[b] : -1;
         a.row0_h = d.kv_row_off_host ? d.kv_row_off_host[b] : 0;
-        tree_attn_bf16_kernel<<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + the loader
+        if (a.ctx_h >= 0)  // 4 computing waves + 4 loaders per workgroup
+            tree_attn_bf16_kernel<true><<<kGridWG, kThreads, 0, stream>>>(a);
+        else
+            tree_attn_bf16_kernel<false><<<kGridWG, kThreads, 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int merge_wg = 8 * ((d.n_kv_heads * RG + 7) / 8) * kRowBlocks;
-        tree_attn_merge_kernel<<<merge_wg, 256, 0, stream>>>(a, kGridWG);
+        if (a.ctx_h >= 0)
+            tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(a, kGridWG);
+        else
+            tree_attn_merge_kernel<false><<<merge_wg, 256, 0, stream>>>(a, kGridWG);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
