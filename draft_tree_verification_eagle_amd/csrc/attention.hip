@@ -150,8 +150,6 @@ __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
-// Barrier for LDS traffic (the K/V loads stay in flight).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Loader wave: wait until at most `tiles_after` tiles' loads (0 or 1) are still
 // in flight; loads complete in issue order, so everything issued before them has
 // landed.

@@ -239,4 +239,8 @@ __device__ __forceinline__ double decision_uniform(uint64_t seed, uint64_t step,
 
 constexpr uint32_t kBonusSlot = 0xFFFFFFFFu;
 
+// Workgroup barrier that orders LDS traffic only: outstanding global loads and
+// stores stay in flight (__syncthreads would also wait for every store to complete).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace eagle

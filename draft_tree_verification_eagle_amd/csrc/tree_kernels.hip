@@ -30,7 +30,8 @@ constexpr int kChunk = kChunkThreads * kChunkPerLane;  // 1024 tokens
 
 __global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
     const float* __restrict__ logits, int V, int rows, int k, int C, uint64_t* __restrict__ ckeys,
-    float* __restrict__ cmax, double* __restrict__ csum) {
+    float* __restrict__ cmax, double* __restrict__ csum, int layer, int cap, int m,
+    const int32_t* __restrict__ frontier, const float* __restrict__ value, float* __restrict__ fval_out) {
     __shared__ uint64_t s_wl[kChunkWaves][EAGLE_MAX_TOPK];  // each wave's top-k, best first
     __shared__ double s_ws[kChunkWaves];                     // each wave's sum of exp(z - wave max)
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -38,6 +39,12 @@ __global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
     const size_t row = (size_t)b * rows + j;
     const float* z = logits + row * (size_t)V;
     const int t0 = c * kChunk + wid * (kWave * kChunkPerLane);
+    // chunk 0's workgroup also gathers the value of draft row j's frontier node for
+    // the merge kernel (a dependent pair of loads, off that kernel's critical path)
+    if (c == 0 && tid == 0 && layer > 1) {
+        const int f = frontier[(size_t)b * m + j];
+        fval_out[(size_t)b * rows + j] = value[(size_t)b * cap + f];
+    }
     float zv[kChunkPerLane];
     uint64_t key[kChunkPerLane];
 #pragma unroll
@@ -121,6 +128,7 @@ constexpr int kFinishWaves = kFinishThreads / kWave;
 constexpr int kMergeLdsKeys = 8192;  // 64 KB of chunk lists per pass
 constexpr int kMaxChunkHeads = 4;    // chunk lists per lane: C <= 256
 constexpr int kFrontierRounds = 32;  // up to this many frontier nodes: one wave selects them
+constexpr int kCopyBatch = 8;       // chunk-list loads per lane in flight together
 static_assert((EAGLE_MAX_VOCAB + kChunk - 1) / kChunk <= kMaxChunkHeads * kWave, "chunk lists per lane");
 static_assert(((EAGLE_MAX_VOCAB + kChunk - 1) / kChunk) * EAGLE_MAX_TOPK <= kMergeLdsKeys, "one row's lists fit");
 
@@ -130,11 +138,13 @@ static_assert(((EAGLE_MAX_VOCAB + kChunk - 1) / kChunk) * EAGLE_MAX_TOPK <= kMer
 template <int NH>
 __device__ __forceinline__ uint64_t merge_chunk_lists(const uint64_t* lists, int C, int k, int lane) {
     int pos[NH];
-    uint64_t h[NH];
+    uint64_t h[NH], nx[NH];  // head and the entry after it (read ahead, so an advance waits on no LDS read)
 #pragma unroll
     for (int u = 0; u < NH; ++u) {
         pos[u] = 0;
-        h[u] = lane + u * kWave < C ? lists[(lane + u * kWave) * k] : 0;
+        const bool own = lane + u * kWave < C;
+        h[u] = own ? lists[(lane + u * kWave) * k] : 0;
+        nx[u] = own && k > 1 ? lists[(lane + u * kWave) * k + 1] : 0;
     }
     uint64_t mykey = 0;
     for (int r = 0; r < k; ++r) {
@@ -146,7 +156,8 @@ __device__ __forceinline__ uint64_t merge_chunk_lists(const uint64_t* lists, int
         for (int u = 0; u < NH; ++u)
             if (best != 0 && h[u] == best) {  // keys are unique: one owner, which moves to its next key
                 ++pos[u];
-                h[u] = pos[u] < k ? lists[(lane + u * kWave) * k + pos[u]] : 0;
+                h[u] = nx[u];
+                nx[u] = pos[u] + 1 < k ? lists[(lane + u * kWave) * k + pos[u] + 1] : 0;
             }
         if (lane == r) mykey = best;
     }
@@ -183,10 +194,30 @@ __device__ __forceinline__ uint64_t frontier_pick(const float* s_val, int L, int
     return select_top<NQ>(cand, keep, lane);
 }
 
+// The first `keep` of L <= kRankNodes new nodes by rank: eight threads per node count
+// the keys above it (keys are unique, so ranks are distinct) and the node of rank r
+// lands in frontier slot r.  All threads of the workgroup take part.
+constexpr int kRankNodes = kFinishThreads / 8;
+__device__ __forceinline__ void frontier_by_rank(const float* s_val, int L, int base, int keep, int tid,
+                                                 int32_t* __restrict__ frontier_out) {
+    const int i = tid >> 3, part = tid & 7;
+    auto key_of = [&](int x) {
+        return ((uint64_t)float_order_key(s_val[x]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(base + x));
+    };
+    const uint64_t mine = i < L ? key_of(i) : 0;
+    uint32_t above = 0;
+    for (int x = part; x < L; x += 8) above += key_of(x) > mine;
+    above += dpp_u32<kDppXor1>(above);        // the eight counts of node i sit in
+    above += dpp_u32<kDppXor2>(above);        // lanes 8q .. 8q + 7 of one row
+    above += dpp_u32<kDppHalfMirror>(above);
+    if (part == 0 && i < L && (int)above < keep) frontier_out[above] = base + i;
+}
+
 __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
     int rows, int k, int C, int layer, int depth_total, const uint64_t* __restrict__ ckeys,
     const float* __restrict__ cmax, const double* __restrict__ csum,
-    const int32_t* __restrict__ root_token, int cap, int m, int32_t* __restrict__ token,
+    const int32_t* __restrict__ root_token, const float* __restrict__ fval_in, int cap, int m,
+    int32_t* __restrict__ token,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth, float* __restrict__ value,
     int32_t* __restrict__ frontier, int32_t* __restrict__ n_nodes) {
     __shared__ uint64_t lists[kMergeLdsKeys];
@@ -218,7 +249,6 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
         int f = 0;
         float fval = 0.0f;
         if (active) {
-            for (int i = lane; i < per_row; i += kWave) mine[i] = ckeys[row * per_row + i];
 #pragma unroll
             for (int u = 0; u < kMaxChunkHeads; ++u) {
                 const int cu = lane + u * kWave;
@@ -227,7 +257,22 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
             }
             if (layer != 1) {
                 f = frontier[(size_t)b * m + j];
-                fval = value[(size_t)b * cap + f];
+                fval = fval_in[(size_t)b * rows + j];
+            }
+            // the lists: a batch of loads in flight before any LDS store (a load-store
+            // loop would pay one memory round trip per 64 keys)
+            for (int i0 = lane; i0 < per_row; i0 += kCopyBatch * kWave) {
+                uint64_t t[kCopyBatch];
+#pragma unroll
+                for (int q = 0; q < kCopyBatch; ++q) {
+                    const int i = i0 + q * kWave;
+                    t[q] = i < per_row ? ckeys[row * per_row + i] : 0;
+                }
+#pragma unroll
+                for (int q = 0; q < kCopyBatch; ++q) {
+                    const int i = i0 + q * kWave;
+                    if (i < per_row) mine[i] = t[q];
+                }
             }
         }
         __syncthreads();
@@ -256,9 +301,13 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
                 s_val[j * k + lane] = val;
             }
         }
-        __syncthreads();  // the lists area is reused by the next pass; every frontier entry read
+        // the lists area is reused by the next pass and s_val is read below; every
+        // frontier entry of this pass was read (its parent ids are in the stores)
+        barrier_lds();
     }
-    if (layer < depth_total && (L < m ? L : m) <= kFrontierRounds) {
+    if (layer < depth_total && L <= kRankNodes) {
+        frontier_by_rank(s_val, L, base, L < m ? L : m, tid, frontier + (size_t)b * m);
+    } else if (layer < depth_total && (L < m ? L : m) <= kFrontierRounds) {
         // frontier = the first min(m, L) new nodes in (value desc, id asc): by that
         // many rounds of a wave maximum over the layer
         if (wid == 0) {
@@ -379,9 +428,10 @@ __global__ __launch_bounds__(64) void mask_kernel(int cap, int n, const int32_t*
 // Host launchers.
 // ---------------------------------------------------------------------------
 // Expand workspace: per (sequence, draft row, chunk) the chunk's k keys, its max
-// logit and its fp64 exp sum; draft rows <= m.
+// logit and its fp64 exp sum; per (sequence, draft row) the frontier node's value;
+// draft rows <= m.
 struct ExpandWs {
-    size_t keys, max, sum, total;
+    size_t keys, max, sum, fval, total;
 };
 static ExpandWs expand_ws(const eagle_tree_cfg& cfg) {
     const size_t C = (size_t)expand_chunks(cfg.vocab);
@@ -390,7 +440,8 @@ static ExpandWs expand_ws(const eagle_tree_cfg& cfg) {
     w.keys = 0;
     w.max = (cells * (size_t)cfg.topk * 8 + 255) & ~(size_t)255;
     w.sum = w.max + ((cells * 4 + 255) & ~(size_t)255);
-    w.total = w.sum + cells * 8;
+    w.fval = w.sum + ((cells * 8 + 255) & ~(size_t)255);
+    w.total = w.fval + (size_t)cfg.batch * (size_t)(cfg.m > 0 ? cfg.m : 1) * 4;
     return w;
 }
 
@@ -406,12 +457,13 @@ hipError_t launch_expand(const eagle_tree_cfg& cfg, int layer, int rows, int cap
     uint64_t* ckeys = (uint64_t*)(ws + w.keys);
     float* cmax = (float*)(ws + w.max);
     double* csum = (double*)(ws + w.sum);
-    expand_chunk_kernel<<<dim3(C, rows, cfg.batch), kChunkThreads, 0, stream>>>(logits, cfg.vocab, rows, k,
-                                                                               C, ckeys, cmax, csum);
+    float* fval = (float*)(ws + w.fval);
+    expand_chunk_kernel<<<dim3(C, rows, cfg.batch), kChunkThreads, 0, stream>>>(
+        logits, cfg.vocab, rows, k, C, ckeys, cmax, csum, layer, cap, cfg.m, st.frontier, st.value, fval);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     expand_finish_kernel<<<cfg.batch, kFinishThreads, 0, stream>>>(
-        rows, k, C, layer, cfg.depth, ckeys, cmax, csum, root_token, cap, cfg.m, st.token, st.parent,
+        rows, k, C, layer, cfg.depth, ckeys, cmax, csum, root_token, fval, cap, cfg.m, st.token, st.parent,
         st.depth, st.value, st.frontier, st.n_nodes);
     return hipGetLastError();
 }
