@@ -50,8 +50,12 @@ def lib():
         L.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, i64, P, f64, i32, P, P, P, P]
         L.orc_verify_greedy.argtypes = [i32, i32, P, P, P, i32, P, P, P]
         L.orc_verify_sampled.argtypes = [i32, i32, P, P, P, i32, f32, u64, u64, i32, P, P, P, P, i32, P]
+        L.orc_flatten_static.argtypes = [i32, P, i32, P, P, P]
+        L.orc_rope.argtypes = [i32, i32, i32, P, f64, P, P]
+        L.orc_kv_commit.argtypes = [i32, i32, i32, P, i32, i64, i64, i64, P, P]
         for f in ("orc_tree_shape", "orc_expand", "orc_rerank", "orc_flatten", "orc_attention",
-                  "orc_verify_greedy", "orc_verify_sampled"):
+                  "orc_verify_greedy", "orc_verify_sampled", "orc_flatten_static", "orc_rope",
+                  "orc_kv_commit"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -175,6 +179,43 @@ def verify_sampled(target, flat_token, flat_parent, max_depth: int, temperature:
     if rc:
         raise ValueError("temperature must be > 0")
     return int(al[0]), ap, ot, tr[: min(int(nt[0]), max_trace)]
+
+
+def flatten_static(parent, ctx_len: int):
+    """Caller-given flattened tree: parent [T] (parent[0] = -1, parent[i] < i).
+    Returns dict(flat_depth, position, mask [T][T] uint8)."""
+    par = _c(parent, np.int32); T = len(par)
+    dep = np.zeros(T, np.int32); pos = np.zeros(T, np.int32); mask = np.zeros((T, T), np.uint8)
+    if lib().orc_flatten_static(T, _p(par), int(ctx_len), _p(dep), _p(pos), _p(mask)):
+        raise ValueError("parent array is not a flattened tree")
+    return dict(flat_depth=dep, position=pos, mask=mask)
+
+
+def rope(x, positions, base: float = 10000.0):
+    """Half-split rotary of x [rows][H][D] (widened exactly to fp32) at positions
+    [rows]; returns fp64 [rows][H][D]."""
+    xf = _c(x, np.float32); rows, H, D = xf.shape
+    pos = _c(positions, np.int32)
+    out = np.zeros((rows, H, D))
+    if lib().orc_rope(rows, H, D, _p(pos), float(base), _p(xf), _p(out)):
+        raise ValueError("head_dim must be even")
+    return out
+
+
+def kv_commit(cache, ctx_len: int, T: int, accept_len: int, path, row0: int = 0):
+    """One sequence, one cache array [heads][rows][D] of any dtype, updated in place.
+    Returns the new context length."""
+    assert cache.flags["C_CONTIGUOUS"]
+    H, rows = cache.shape[0], cache.shape[1]
+    row_bytes = cache.strides[1]
+    pa = _c(np.asarray(path)[:max(accept_len, 0)], np.int32)
+    if pa.size == 0:
+        pa = np.zeros(1, np.int32)
+    nc = np.zeros(1, np.int32)
+    if lib().orc_kv_commit(int(T), int(ctx_len), int(accept_len), _p(pa), H, rows, int(row0), row_bytes,
+                           cache.ctypes.data_as(C.c_void_p), _p(nc)):
+        raise ValueError("accepted path is not a strictly increasing run of tree rows")
+    return int(nc[0])
 
 
 # ---------------------------------------------------------------------------

@@ -458,4 +458,98 @@ int orc_verify_sampled(int T, int V, const float* target, const int* flat_token,
     return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Flatten a caller-given static tree (EAGLE-2 page, opening paragraphs: EAGLE and
+// Medusa use a fixed draft-tree shape; the passage after the two stages: the
+// flattened tree's ancestor-only mask and positions).  The tree arrives already
+// flattened: parent[0] = -1 and 0 <= parent[i] < i for every other row, so row
+// order is topological.  depth(i) = depth(parent(i)) + 1; position = ctx_len +
+// depth; mask[i][j] = 1 iff row j lies on the root-to-row-i path (i included).
+// Returns 0, or -1 if the parent array is not of that form.
+// ---------------------------------------------------------------------------
+int orc_flatten_static(int T, const int* parent, int ctx_len, int* flat_depth, int* position,
+                       unsigned char* mask) {
+    if (T < 1 || parent[0] != -1) return -1;
+    for (int i = 1; i < T; ++i)
+        if (parent[i] < 0 || parent[i] >= i) return -1;
+    for (int i = 0; i < T; ++i) {
+        int d = 0;
+        for (int r = i; parent[r] >= 0; r = parent[r]) ++d;
+        flat_depth[i] = d;
+        position[i] = ctx_len + d;
+    }
+    std::memset(mask, 0, (size_t)T * T);
+    for (int i = 0; i < T; ++i)
+        for (int r = i; r >= 0; r = parent[r]) mask[(size_t)i * T + r] = 1;
+    return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Rotary position encoding at the tree positions (EAGLE-2 page, passage after
+// the two stages: the positions of the flattened tokens are adjusted so that
+// each matches the position it would have in autoregressive decoding).  The
+// encoding itself is the rotary one of the LLaMA family the workloads are shaped
+// after, in its half-split form: for d < D/2, with theta = pos * base^(-2d/D),
+// the pair (x[d], x[d + D/2]) is rotated by theta:
+//   out[d]       = x[d] cos(theta) - x[d + D/2] sin(theta)
+//   out[d + D/2] = x[d + D/2] cos(theta) + x[d] sin(theta)
+// computed in fp64.  x: [rows][H][D], pos: [rows]; out: [rows][H][D] fp64.
+// Returns 0, or -1 for an odd or non-positive D.
+// ---------------------------------------------------------------------------
+int orc_rope(int rows, int H, int D, const int* pos, double base, const float* x, double* out) {
+    if (D < 2 || D % 2 != 0 || H < 1 || rows < 0) return -1;
+    const int half = D / 2;
+    for (int i = 0; i < rows; ++i) {
+        for (int h = 0; h < H; ++h) {
+            const float* xi = x + ((size_t)i * H + h) * D;
+            double* oi = out + ((size_t)i * H + h) * D;
+            for (int d = 0; d < half; ++d) {
+                const double theta = (double)pos[i] * std::pow(base, -2.0 * d / D);
+                const double c = std::cos(theta), s = std::sin(theta);
+                const double a = xi[d], b = xi[d + half];
+                oi[d] = a * c - b * s;
+                oi[d + half] = b * c + a * s;
+            }
+        }
+    }
+    return 0;
+}
+
+// ---------------------------------------------------------------------------
+// KV commit of the accepted path (EAGLE-2 page, passage after the two stages:
+// the verified tokens must stand exactly as autoregressive decoding would have
+// left them; CSDN page 1.1: the accepted draft tokens are emitted as output).
+// One sequence, one cache (K or V): rows are row_bytes wide, head g's row r at
+// byte offset (g * head_rows + row0 + r) * row_bytes.  The tree rows sit at
+// ctx_len .. ctx_len + T - 1 in flattened order, row ctx_len being the root (the
+// token emitted last step).  With accepted flattened rows path[0..a-1], the
+// committed cache holds, at rows ctx_len + 1 + j, the rows that sat at
+// ctx_len + path[j] -- all source rows are read before any is written.  Rows
+// outside ctx_len + 1 .. ctx_len + a are left as they were.  The new context
+// length (root and accepted rows kept; the bonus token is the next root) is
+// returned through new_ctx.  Returns 0, or -1 if the path is not strictly
+// increasing inside 1 .. T - 1 (a root path in flattened order always is).
+// ---------------------------------------------------------------------------
+int orc_kv_commit(int T, int ctx_len, int accept_len, const int* path, int n_heads,
+                  long long head_rows, long long row0, long long row_bytes, unsigned char* cache,
+                  int* new_ctx) {
+    if (accept_len < 0 || accept_len > T - 1) return -1;
+    for (int j = 0; j < accept_len; ++j) {
+        if (path[j] < 1 || path[j] >= T) return -1;
+        if (j > 0 && path[j] <= path[j - 1]) return -1;
+    }
+    std::vector<unsigned char> rows((size_t)accept_len * row_bytes);
+    for (int g = 0; g < n_heads; ++g) {
+        unsigned char* head = cache + (size_t)g * head_rows * row_bytes;
+        for (int j = 0; j < accept_len; ++j)
+            std::memcpy(&rows[(size_t)j * row_bytes],
+                        head + (size_t)(row0 + ctx_len + path[j]) * row_bytes, row_bytes);
+        for (int j = 0; j < accept_len; ++j)
+            std::memcpy(head + (size_t)(row0 + ctx_len + 1 + j) * row_bytes,
+                        &rows[(size_t)j * row_bytes], row_bytes);
+    }
+    *new_ctx = ctx_len + 1 + accept_len;
+    return 0;
+}
+
 }  // extern "C"
