@@ -42,6 +42,12 @@ class AttnDesc(C.Structure):
                 ("ctx_len_host", C.c_void_p), ("kv_row_off_host", C.c_void_p)]
 
 
+class CommitDesc(C.Structure):
+    _fields_ = [("dtype", C.c_int), ("batch", C.c_int32), ("T", C.c_int32), ("depth", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("n_layers", C.c_int32),
+                ("ctx_len", C.c_void_p), ("kv_row_off", C.c_void_p), ("kv_rows_total", C.c_int64)]
+
+
 def load_library(path: str = _LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
@@ -58,6 +64,9 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
     L.eagle_verify_workspace.argtypes = [P]; L.eagle_verify_workspace.restype = sz
     L.eagle_verify.argtypes = [P, P, P, P, C.c_float, u64, u64, P, P, P, P, sz, P]
     L.eagle_verify.restype = C.c_int
+    L.eagle_tree_mask_static.argtypes = [i32, i32, P, P, P, P, P, P]; L.eagle_tree_mask_static.restype = C.c_int
+    L.eagle_tree_rope.argtypes = [P, P, C.c_double, P, P, P]; L.eagle_tree_rope.restype = C.c_int
+    L.eagle_kv_commit.argtypes = [P, P, P, P, P, P, P]; L.eagle_kv_commit.restype = C.c_int
     L.eagle_status_string.argtypes = [C.c_int]; L.eagle_status_string.restype = C.c_char_p
     return L
 
@@ -198,3 +207,32 @@ def eagle_verify(cfg: TreeCfg, target_logits, flat_token, flat_parent, temperatu
         C.byref(cfg), _ptr(target_logits), _ptr(flat_token), _ptr(flat_parent), float(temperature),
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(step) & 0xFFFFFFFFFFFFFFFF, _ptr(accept_len), _ptr(accept_path),
         _ptr(out_tokens), _ptr(workspace), nbytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Around the step: static-tree mask, rotary at the tree positions, KV commit.
+# ---------------------------------------------------------------------------
+def eagle_tree_mask_static(batch: int, T: int, flat_parent, ctx_len, flat_depth, position, mask, stream=None):
+    _check("eagle_tree_mask_static", _lib.eagle_tree_mask_static(
+        int(batch), int(T), _ptr(flat_parent), _ptr(ctx_len), _ptr(flat_depth), _ptr(position), _ptr(mask),
+        _stream(stream)))
+
+
+def eagle_tree_rope(desc: AttnDesc, position, base: float, q, k_cache, stream=None):
+    _check("eagle_tree_rope", _lib.eagle_tree_rope(C.byref(desc), _ptr(position), float(base), _ptr(q),
+                                                   _ptr(k_cache), _stream(stream)))
+
+
+def make_commit_desc(dtype: int, batch: int, T: int, depth: int, n_kv_heads: int, head_dim: int,
+                     n_layers: int, ctx_len, kv_row_off, kv_rows_total: int) -> CommitDesc:
+    return CommitDesc(dtype, batch, T, depth, n_kv_heads, head_dim, n_layers, _ptr(ctx_len), _ptr(kv_row_off),
+                      int(kv_rows_total))
+
+
+def eagle_kv_commit(desc: CommitDesc, accept_len, accept_path, k_layers, v_layers, new_ctx_len, stream=None):
+    """k_layers / v_layers: sequences of device tensors (one cache per layer)."""
+    n = len(k_layers)
+    KA = (C.c_void_p * max(n, 1))(*[_ptr(t) for t in k_layers])
+    VA = (C.c_void_p * max(n, 1))(*[_ptr(t) for t in v_layers])
+    _check("eagle_kv_commit", _lib.eagle_kv_commit(C.byref(desc), _ptr(accept_len), _ptr(accept_path), KA, VA,
+                                                   _ptr(new_ctx_len), _stream(stream)))

@@ -165,6 +165,53 @@ int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const in
                                          step, accept_len, accept_path, out_tokens, workspace, stream));
 }
 
+int eagle_tree_mask_static(int32_t batch, int32_t T, const int32_t* flat_parent, const int32_t* ctx_len,
+                           int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream) {
+    if (batch < 0 || T < 1) return EAGLE_ERR_INVALID_ARG;
+    if (batch > EAGLE_MAX_BATCH || T > EAGLE_MAX_TREE_ROWS) return EAGLE_ERR_UNSUPPORTED;
+    if (batch == 0) return EAGLE_OK;
+    if (!flat_parent || !ctx_len || !flat_depth || !position || !mask) return EAGLE_ERR_INVALID_ARG;
+    return from_hip(eagle::launch_mask_static(batch, T, flat_parent, ctx_len, flat_depth, position, mask,
+                                              stream));
+}
+
+int eagle_tree_rope(const eagle_attn_desc* desc, const int32_t* position, double base, void* q,
+                    void* k_cache, hipStream_t stream) {
+    const eagle_attn_desc* d = desc;
+    if (!d || d->batch < 0 || d->T < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 2 ||
+        d->head_dim % 2 != 0 || d->kv_rows_total < 0 || !(base > 0.0) || isinf(base))
+        return EAGLE_ERR_INVALID_ARG;
+    if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
+    if (d->T > EAGLE_MAX_TREE_ROWS || d->head_dim > 256 || d->batch > EAGLE_MAX_BATCH) return EAGLE_ERR_UNSUPPORTED;
+    if (d->batch == 0 || (!q && !k_cache)) return EAGLE_OK;
+    if (!position || (k_cache && (!d->ctx_len || !d->kv_row_off))) return EAGLE_ERR_INVALID_ARG;
+    return from_hip(eagle::launch_rope(*d, position, base, q, k_cache, stream));
+}
+
+int eagle_kv_commit(const eagle_commit_desc* desc, const int32_t* accept_len, const int32_t* accept_path,
+                    void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len, hipStream_t stream) {
+    const eagle_commit_desc* d = desc;
+    if (!d || d->batch < 0 || d->T < 1 || d->depth < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+        d->n_layers < 0 || d->kv_rows_total < 0)
+        return EAGLE_ERR_INVALID_ARG;
+    if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
+    const int align = d->dtype == EAGLE_BF16 ? 8 : 4;
+    if (d->T > EAGLE_MAX_TREE_ROWS || d->depth > 255 || d->head_dim > 256 || d->head_dim % align != 0 ||
+        d->batch > EAGLE_MAX_BATCH || d->n_kv_heads > 65535)
+        return EAGLE_ERR_UNSUPPORTED;
+    if (d->batch == 0) return EAGLE_OK;
+    if (!accept_len || !accept_path || !new_ctx_len || !d->ctx_len || !d->kv_row_off ||
+        (const void*)new_ctx_len == (const void*)d->ctx_len)
+        return EAGLE_ERR_INVALID_ARG;
+    if (d->n_layers > 0 && (!k_layers || !v_layers)) return EAGLE_ERR_INVALID_ARG;
+    for (int l = 0; l < d->n_layers; ++l) {
+        if (!k_layers[l] || !v_layers[l] || ((uintptr_t)k_layers[l] & 15) || ((uintptr_t)v_layers[l] & 15))
+            return EAGLE_ERR_INVALID_ARG;
+    }
+    return from_hip(eagle::launch_kv_commit(*d, accept_len, accept_path, k_layers, v_layers, new_ctx_len,
+                                            stream));
+}
+
 const char* eagle_status_string(int status) {
     switch (status) {
         case EAGLE_OK: return "ok";

@@ -1,0 +1,237 @@
+// Kernels around the verification step: the mask of a caller-given static tree,
+// rotary position encoding of the tree rows at their positions, and the KV
+// commit of the accepted path.  All three are small (tens of KB to a few MB per
+// step) and latency-bound; each is one launch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launchers.hpp"
+
+namespace eagle {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Static tree: one wave per sequence, lane i = row i.  Row i's ancestors are
+// found by walking parent links; a walk that meets a parent entry which is not an
+// earlier row (or a root entry other than -1) marks the row invalid.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void mask_static_kernel(int T, const int32_t* __restrict__ flat_parent,
+                                                         const int32_t* __restrict__ ctx_len,
+                                                         int32_t* __restrict__ flat_depth,
+                                                         int32_t* __restrict__ position,
+                                                         uint64_t* __restrict__ mask) {
+    __shared__ int32_t par[EAGLE_MAX_TREE_ROWS];
+    const int b = blockIdx.x, i = threadIdx.x;
+    if (i < T) par[i] = flat_parent[(size_t)b * T + i];
+    __syncthreads();
+    if (i >= T) return;
+    uint64_t bits = 0;
+    int depth = 0;
+    bool ok = true;
+    int r = i;
+    // each step moves to a strictly earlier row, so the walk ends within T steps
+    while (true) {
+        bits |= 1ull << r;
+        const int p = par[r];
+        if (r == 0) {
+            ok = (p == -1);
+            break;
+        }
+        if (p < 0 || p >= r) {
+            ok = false;
+            break;
+        }
+        r = p;
+        ++depth;
+    }
+    const size_t o = (size_t)b * T + i;
+    flat_depth[o] = ok ? depth : -1;
+    position[o] = ok ? ctx_len[b] + depth : -1;
+    mask[o] = ok ? bits : 0ull;
+}
+
+// ---------------------------------------------------------------------------
+// Rotary position encoding of the tree rows.  One workgroup per (tree row,
+// sequence): the row's head_dim/2 cosines and sines (fp64) go to LDS, then the
+// workgroup rotates the row's query heads and its KV heads' tree row in place.
+// Consecutive threads take consecutive coordinates of a head, so every load and
+// store of a head row is one coalesced sweep.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double load_elt(const float* p) { return (double)*p; }
+__device__ __forceinline__ double load_elt(const uint16_t* p) {
+    return (double)__uint_as_float((uint32_t)*p << 16);
+}
+__device__ __forceinline__ void store_elt(float* p, double x) { *p = (float)x; }
+__device__ __forceinline__ void store_elt(uint16_t* p, double x) {
+    uint32_t u = __float_as_uint((float)x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        *p = (uint16_t)((u >> 16) | 0x40u);  // NaN stays a (quiet) NaN
+        return;
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
+    *p = (uint16_t)(u >> 16);
+}
+
+template <typename Elt>
+__device__ __forceinline__ void rotate_pair(Elt* row, int d, int half, double c, double s) {
+    const double x = load_elt(row + d), y = load_elt(row + d + half);
+    store_elt(row + d, x * c - y * s);
+    store_elt(row + d + half, y * c + x * s);
+}
+
+template <typename Elt>
+__global__ __launch_bounds__(256) void rope_kernel(int T, int Hq, int Hkv, int D,
+                                                   const int32_t* __restrict__ position,
+                                                   const int32_t* __restrict__ ctx_len,
+                                                   const int64_t* __restrict__ kv_row_off,
+                                                   int64_t kv_rows_total, double base, Elt* q, Elt* k) {
+    __shared__ double cs[128], sn[128];
+    const int i = blockIdx.x, b = blockIdx.y;
+    const int half = D >> 1;
+    const double p = (double)position[(size_t)b * T + i];
+    for (int d = threadIdx.x; d < half; d += blockDim.x) {
+        const double theta = p * pow(base, -2.0 * d / D);
+        double s, c;
+        sincos(theta, &s, &c);
+        cs[d] = c;
+        sn[d] = s;
+    }
+    __syncthreads();
+    if (q) {
+        Elt* qr = q + ((size_t)b * T + i) * (size_t)Hq * D;
+        for (int e = threadIdx.x; e < Hq * half; e += blockDim.x) {
+            const int h = e / half, d = e - h * half;
+            rotate_pair(qr + (size_t)h * D, d, half, cs[d], sn[d]);
+        }
+    }
+    if (k) {
+        const int64_t row = kv_row_off[b] + (int64_t)ctx_len[b] + i;
+        if (row < 0 || row >= kv_rows_total) return;  // outside the cache: nothing to rotate
+        for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
+            const int h = e / half, d = e - h * half;
+            rotate_pair(k + ((size_t)h * kv_rows_total + row) * D, d, half, cs[d], sn[d]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// KV commit.  One wave per (KV head, layer x {K, V}, sequence).  Accepted rows
+// r_1 < ... < r_a satisfy r_j >= j, and once r_j > j every later r_i > i: the
+// rows that stay put form a prefix, and the rows that move are j0..a.  They are
+// copied in batches of up to 256 16-byte chunks in ascending j: a batch's chunks
+// are all loaded and staged in LDS before the barrier, then stored.  A batch's
+// sources (rows r_j > j) never lie among the rows written by earlier batches
+// (rows < j), and within a batch every load has completed before the barrier, so
+// no row is overwritten before it is read.
+// ---------------------------------------------------------------------------
+constexpr int kCommitChunks = 256;  // 16-byte chunks staged per batch (4 KB of LDS)
+
+struct CommitLayers {
+    char* k[kCommitMaxLayers];
+    char* v[kCommitMaxLayers];
+};
+
+__global__ __launch_bounds__(64) void kv_commit_kernel(int T, int depth, int row_chunks,
+                                                       int64_t kv_rows_total,
+                                                       const int32_t* __restrict__ ctx_len,
+                                                       const int64_t* __restrict__ kv_row_off,
+                                                       const int32_t* __restrict__ accept_len,
+                                                       const int32_t* __restrict__ accept_path,
+                                                       int32_t* __restrict__ new_ctx_len, int write_ctx,
+                                                       CommitLayers L) {
+    __shared__ uint4 stage[kCommitChunks];
+    __shared__ int32_t path[256];
+    const int g = blockIdx.x, layer = blockIdx.y >> 1, is_v = blockIdx.y & 1, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int a = accept_len[b];
+    const int amax = depth < T - 1 ? depth : T - 1;
+    const int64_t ctx = ctx_len[b], off = kv_row_off[b];
+    bool ok = a >= 0 && a <= amax && ctx >= 0 && off >= 0 && off + ctx + T <= kv_rows_total;
+    int bad = 0;
+    if (ok) {
+        for (int j = lane; j < a; j += 64) {
+            const int r = accept_path[(size_t)b * depth + j];
+            path[j] = r;
+            bad |= (r < 1 || r >= T);
+        }
+    }
+    __syncthreads();
+    if (ok) {
+        for (int j = 1 + lane; j < a; j += 64) bad |= (path[j] <= path[j - 1]);
+    }
+    const int any_bad = __syncthreads_or(bad);  // every lane reaches this barrier
+    ok = ok && !any_bad;
+    if (write_ctx && g == 0 && blockIdx.y == 0 && lane == 0) new_ctx_len[b] = ok ? (int32_t)(ctx + 1 + a) : -1;
+    if (!ok) return;
+    int stay = 0;  // rows with r_j == j form a prefix
+    while (stay < a && path[stay] == stay + 1) ++stay;
+    const int moved = a - stay;
+    if (moved == 0) return;
+    char* cache = is_v ? L.v[layer] : L.k[layer];
+    if (!cache) return;  // launched only to report the new context lengths
+    const size_t row_bytes = (size_t)row_chunks * 16;
+    char* base = cache + ((size_t)g * kv_rows_total + off + ctx) * row_bytes;
+    const int total = moved * row_chunks;
+    for (int e0 = 0; e0 < total; e0 += kCommitChunks) {
+        const int n = total - e0 < kCommitChunks ? total - e0 : kCommitChunks;
+        for (int e = lane; e < n; e += 64) {
+            const int idx = e0 + e;
+            const int j = stay + idx / row_chunks, c = idx - (idx / row_chunks) * row_chunks;
+            stage[e] = *reinterpret_cast<const uint4*>(base + (size_t)path[j] * row_bytes + (size_t)c * 16);
+        }
+        __syncthreads();
+        for (int e = lane; e < n; e += 64) {
+            const int idx = e0 + e;
+            const int j = stay + idx / row_chunks, c = idx - (idx / row_chunks) * row_chunks;
+            *reinterpret_cast<uint4*>(base + (size_t)(j + 1) * row_bytes + (size_t)c * 16) = stage[e];
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mask_static(int batch, int T, const int32_t* flat_parent, const int32_t* ctx_len,
+                              int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream) {
+    mask_static_kernel<<<batch, 64, 0, stream>>>(T, flat_parent, ctx_len, flat_depth, position, mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope(const eagle_attn_desc& d, const int32_t* position, double base, void* q, void* k,
+                       hipStream_t stream) {
+    const dim3 grid(d.T, d.batch);
+    if (d.dtype == EAGLE_BF16)
+        rope_kernel<uint16_t><<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position,
+                                                         d.ctx_len, d.kv_row_off, d.kv_rows_total, base,
+                                                         (uint16_t*)q, (uint16_t*)k);
+    else
+        rope_kernel<float><<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position,
+                                                      d.ctx_len, d.kv_row_off, d.kv_rows_total, base,
+                                                      (float*)q, (float*)k);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_commit(const eagle_commit_desc& d, const int32_t* accept_len, const int32_t* accept_path,
+                            void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len,
+                            hipStream_t stream) {
+    const int elt = d.dtype == EAGLE_BF16 ? 2 : 4;
+    const int row_chunks = d.head_dim * elt / 16;
+    // with no layers one launch still writes new_ctx_len (null cache pointers: no copies)
+    for (int l0 = 0; l0 == 0 || l0 < d.n_layers; l0 += kCommitMaxLayers) {
+        const int nl = d.n_layers - l0 < kCommitMaxLayers ? d.n_layers - l0 : kCommitMaxLayers;
+        CommitLayers L{};
+        for (int l = 0; l < nl; ++l) {
+            L.k[l] = (char*)k_layers[l0 + l];
+            L.v[l] = (char*)v_layers[l0 + l];
+        }
+        const dim3 grid(nl > 0 ? d.n_kv_heads : 1, nl > 0 ? 2 * nl : 1, d.batch);
+        kv_commit_kernel<<<grid, 64, 0, stream>>>(d.T, d.depth, row_chunks, d.kv_rows_total, d.ctx_len,
+                                                  d.kv_row_off, accept_len, accept_path, new_ctx_len,
+                                                  l0 == 0 ? 1 : 0, L);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace eagle

@@ -41,4 +41,14 @@ hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const i
                          uint64_t step, int32_t* accept_len, int32_t* accept_path,
                          int32_t* out_tokens, void* workspace, hipStream_t stream);
 
+// Around the step: static-tree mask, rotary at the tree positions, KV commit.
+constexpr int kCommitMaxLayers = 64;  // layers per commit launch (their pointers ride in the arguments)
+hipError_t launch_mask_static(int batch, int T, const int32_t* flat_parent, const int32_t* ctx_len,
+                              int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream);
+hipError_t launch_rope(const eagle_attn_desc& d, const int32_t* position, double base, void* q, void* k,
+                       hipStream_t stream);
+hipError_t launch_kv_commit(const eagle_commit_desc& d, const int32_t* accept_len, const int32_t* accept_path,
+                            void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len,
+                            hipStream_t stream);
+
 }  // namespace eagle

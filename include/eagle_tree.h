@@ -7,6 +7,12 @@
  *   eagle_tree_mask       flatten the kept tree: tokens, parents, positions, ancestor mask
  *   eagle_tree_attention  tree attention of the flattened rows against the KV cache
  *   eagle_verify          lossless acceptance (greedy or sampled) over target logits
+ * and three calls around it:
+ *   eagle_tree_mask_static  positions and ancestor mask of a caller-given fixed tree
+ *                           (the static trees of EAGLE / Medusa), in place of the first three
+ *   eagle_tree_rope         rotary position encoding of the tree rows at their positions
+ *   eagle_kv_commit         move the accepted rows' K/V behind the context, as
+ *                           autoregressive decoding would have left them
  *
  * Pages defining the operations (cited by title and passage):
  *   EAGLE-2 page -- news write-up of "EAGLE-2: Faster Inference of Language Models
@@ -207,6 +213,68 @@ int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const in
                  const int32_t* flat_parent, float temperature, uint64_t seed, uint64_t step,
                  int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
+
+/* Static tree (EAGLE-2 page, opening paragraphs: EAGLE and Medusa draft over a
+ * fixed tree shape; passage after the two stages: ancestor-only mask and
+ * positions of the flattened tree).  In place of expand / rerank / mask, the
+ * caller gives the flattened tree itself: flat_parent [batch][T] int32 device,
+ * row 0 the root (-1), every other row's parent an earlier row.  Outputs as for
+ * eagle_tree_mask: flat_depth and position = ctx_len[b] + depth ([batch][T]
+ * int32) and mask [batch][T] uint64 (bit j of row i set iff row j lies on the
+ * root-to-i path).  The caller's tokens serve as flat_token for attention and
+ * verify unchanged.  A row whose path to the root meets a parent entry that is
+ * not an earlier row (or a root entry other than -1) gets depth -1, position -1
+ * and mask 0; the other rows are unaffected.  1 <= T <= EAGLE_MAX_TREE_ROWS
+ * (otherwise EAGLE_ERR_INVALID_ARG / EAGLE_ERR_UNSUPPORTED). */
+int eagle_tree_mask_static(int32_t batch, int32_t T, const int32_t* flat_parent, const int32_t* ctx_len,
+                           int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream);
+
+/* Rotary position encoding at the tree positions (EAGLE-2 page, passage after
+ * the two stages: the flattened tokens' positions are adjusted so each matches
+ * its position in plain autoregressive decoding).  In place, for sequence b and
+ * tree row i at p = position[b][i] (from eagle_tree_mask or eagle_tree_mask_static):
+ * every head of q [batch][T][n_q_heads][head_dim] and every KV head's tree row
+ * kv_row_off[b] + ctx_len[b] + i of k_cache [n_kv_heads][kv_rows_total][head_dim].
+ * Half-split form (the LLaMA family's): for d < head_dim / 2 the pair
+ * (x[d], x[d + head_dim/2]) is rotated by theta = p * base^(-2d / head_dim).
+ * Angles, cosines, sines and the rotation are fp64; the result is rounded to
+ * fp32 (nearest even) and, for BF16, then to bf16 (nearest even).  Context rows
+ * are not touched (the cache holds them already rotated).  desc as for
+ * eagle_tree_attention (scale and the host copies unused); q or k_cache may be
+ * NULL to rotate only the other.  head_dim even and <= 256, base > 0 and
+ * finite.  Positions are not checked: p < 0 rotates backwards. */
+int eagle_tree_rope(const eagle_attn_desc* desc, const int32_t* position, double base, void* q,
+                    void* k_cache, hipStream_t stream);
+
+/* KV commit of the accepted path (EAGLE-2 page, passage after the two stages:
+ * verified tokens must stand as autoregressive decoding would have left them;
+ * CSDN page 1.1: the accepted draft tokens are the output).  For sequence b with
+ * accept_len a and accept_path r_1 < ... < r_a (flattened rows, from eagle_verify),
+ * in every layer's K and V cache and every KV head, the row at
+ * kv_row_off[b] + ctx_len[b] + r_j moves to kv_row_off[b] + ctx_len[b] + j
+ * (j = 1..a; every source row is read before any is written).  The root's row
+ * (ctx_len[b]) stays; new_ctx_len[b] = ctx_len[b] + 1 + a, the bonus token being
+ * the next root.  Other rows are not touched.
+ * Layouts: k_layers, v_layers are HOST arrays of n_layers device pointers, each
+ * cache [n_kv_heads][kv_rows_total][head_dim] of dtype; accept_len [batch],
+ * accept_path [batch][depth] int32 device (entries past accept_len unread);
+ * ctx_len [batch] int32, kv_row_off [batch] int64 device; new_ctx_len [batch]
+ * int32 device, which must not alias ctx_len.  Each sequence's rows up to
+ * ctx_len[b] + T must lie inside the cache (not checkable on the host).
+ * A sequence whose accept_len lies outside 0..min(depth, T - 1) or whose path is
+ * not strictly increasing inside 1..T - 1 is not moved and gets new_ctx_len -1.
+ * Supported: head_dim a multiple of 8 (BF16) or 4 (F32), head_dim <= 256, T <= 64,
+ * depth <= 255; the layers are processed 64 to a launch. */
+typedef struct {
+    eagle_dtype dtype;
+    int32_t batch, T, depth, n_kv_heads, head_dim, n_layers;
+    const int32_t* ctx_len;    /* [batch] device */
+    const int64_t* kv_row_off; /* [batch] device */
+    int64_t kv_rows_total;
+} eagle_commit_desc;
+
+int eagle_kv_commit(const eagle_commit_desc* desc, const int32_t* accept_len, const int32_t* accept_path,
+                    void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len, hipStream_t stream);
 
 /* Human-readable name of a status code. */
 const char* eagle_status_string(int status);

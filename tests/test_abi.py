@@ -217,3 +217,75 @@ def test_verify_validation(eb):
     assert call(1.0, FAKE, need - 8) == eb.EAGLE_ERR_WORKSPACE
     assert L.eagle_verify(C.byref(cfg), None, FAKE, FAKE, 0.0, 1, 0, FAKE, FAKE, FAKE, FAKE, need, None) == \
         eb.EAGLE_ERR_INVALID_ARG
+
+
+def test_static_mask_validation(eb):
+    L = eb.lib()
+    f = FAKE
+    assert L.eagle_tree_mask_static(0, 5, f, f, f, f, f, None) == eb.EAGLE_OK  # empty batch: no launch
+    assert L.eagle_tree_mask_static(-1, 5, f, f, f, f, f, None) == eb.EAGLE_ERR_INVALID_ARG
+    assert L.eagle_tree_mask_static(2, 0, f, f, f, f, f, None) == eb.EAGLE_ERR_INVALID_ARG
+    assert L.eagle_tree_mask_static(2, 65, f, f, f, f, f, None) == eb.EAGLE_ERR_UNSUPPORTED
+    assert L.eagle_tree_mask_static(2, 5, None, f, f, f, f, None) == eb.EAGLE_ERR_INVALID_ARG
+    assert L.eagle_tree_mask_static(2, 5, f, f, f, f, None, None) == eb.EAGLE_ERR_INVALID_ARG
+
+
+def test_rope_validation(eb):
+    L = eb.lib()
+    f = FAKE
+
+    def desc(**kw):
+        a = dict(dtype=eb.EAGLE_BF16, batch=1, T=61, n_q_heads=40, n_kv_heads=40, head_dim=128, ctx_len=f,
+                 kv_row_off=f, kv_rows_total=5000)
+        a.update(kw)
+        return eb.make_attn_desc(a["dtype"], a["batch"], a["T"], a["n_q_heads"], a["n_kv_heads"], a["head_dim"],
+                                 None, None, a["kv_rows_total"])
+
+    def call(d, pos=f, base=10000.0, q=f, k=f, ctx=f, off=f):
+        d.ctx_len = ctx; d.kv_row_off = off
+        return L.eagle_tree_rope(C.byref(d), pos, base, q, k, None)
+
+    assert call(desc(), q=None, k=None) == eb.EAGLE_OK  # nothing to rotate
+    assert call(desc(batch=0)) == eb.EAGLE_OK
+    assert call(desc(head_dim=127)) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(desc(head_dim=258)) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(desc(T=65)) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(desc(dtype=7)) == eb.EAGLE_ERR_INVALID_ARG
+    for base in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(desc(), base=base) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(desc(), pos=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(desc(), ctx=None) == eb.EAGLE_ERR_INVALID_ARG  # rotating K needs the cache rows
+    assert L.eagle_tree_rope(None, f, 10000.0, f, f, None) == eb.EAGLE_ERR_INVALID_ARG
+
+
+def test_kv_commit_validation(eb):
+    L = eb.lib()
+    f = FAKE
+    ks = (C.c_void_p * 2)(0x2000, 0x3000)
+    vs = (C.c_void_p * 2)(0x4000, 0x5000)
+
+    def call(dtype=eb.EAGLE_BF16, batch=1, T=61, depth=6, hkv=40, D=128, layers=2, ctx=0x6000, off=0x7000,
+             rows=5000, al=f, ap=f, k=ks, v=vs, out=f):
+        d = eb.CommitDesc(dtype, batch, T, depth, hkv, D, layers, ctx, off, rows)
+        return L.eagle_kv_commit(C.byref(d), al, ap, k, v, out, None)
+
+    assert call(batch=0) == eb.EAGLE_OK
+    assert call(batch=-1) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(T=0) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(depth=0) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(T=65) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(depth=256) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(D=124) == eb.EAGLE_ERR_UNSUPPORTED  # bf16 rows must be whole 16-byte chunks
+    assert call(dtype=eb.EAGLE_F32, D=126) == eb.EAGLE_ERR_UNSUPPORTED  # fp32 rows: head_dim % 4
+    assert call(D=264) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(dtype=5) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(al=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(ap=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(out=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(out=0x6000) == eb.EAGLE_ERR_INVALID_ARG  # new_ctx_len may not alias ctx_len
+    assert call(k=None) == eb.EAGLE_ERR_INVALID_ARG
+    bad = (C.c_void_p * 2)(0x2000, 0x3008)  # not 16-byte aligned
+    assert call(k=bad) == eb.EAGLE_ERR_INVALID_ARG
+    nul = (C.c_void_p * 2)(0x2000, 0)
+    assert call(v=nul) == eb.EAGLE_ERR_INVALID_ARG
+    assert L.eagle_kv_commit(None, f, f, ks, vs, f, None) == eb.EAGLE_ERR_INVALID_ARG
