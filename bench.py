@@ -86,6 +86,96 @@ def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 
             "oracle_attention_GBps": attention_bytes_per_launch(w) / t_layer / 1e9}
 
 
+def _graph_us(fn, reps):
+    """Average GPU time of fn's launches: `reps` calls captured in one HIP graph
+    and replayed, timed with HIP events on the replay stream (no host launch
+    overhead between the kernels)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
+    """Rotary at the tree positions (one call per layer), KV commit of an accepted
+    path (one call for all layers), the static-tree mask (graph replays, HIP
+    events), and the whole decode step with rotary and commit included (eager)."""
+    import torch
+    from draft_tree_verification_eagle_amd import binding as eb
+
+    print("[bench] timing rotary, KV commit, static mask", file=sys.stderr, flush=True)
+    elt = 4 if w.dtype == "f32" else 2
+    # the commit moves the deepest root path of each tree (the longest acceptance
+    # this tree allows, every row of it away from its final place when the path
+    # leaves the first-child chain)
+    fp = vs.flat_parent.cpu().numpy()
+    al = np.zeros(w.batch, np.int32)
+    ap = np.full((w.batch, w.depth), -1, np.int32)
+    moved = 0
+    for b in range(w.batch):
+        path, r = [], w.T - 1
+        while r > 0:
+            path.append(r); r = int(fp[b, r])
+        path = path[::-1]
+        al[b] = len(path); ap[b, :len(path)] = path
+        stay = 0
+        while stay < len(path) and path[stay] == stay + 1:
+            stay += 1
+        moved += len(path) - stay
+    vs.accept_len.copy_(torch.from_numpy(al)); vs.accept_path.copy_(torch.from_numpy(ap))
+    rope_us = _graph_us(lambda: vs.rope(), 2) / vs.n_layers
+    rope_bytes = 2 * (w.batch * w.T * w.n_q_heads + w.batch * w.T * w.n_kv_heads) * w.head_dim * elt
+    commit_us = _graph_us(lambda: vs.commit(), reps)
+    commit_bytes = 2 * 2 * vs.n_layers * w.n_kv_heads * w.head_dim * elt * moved
+    fpd = vs.flat_parent
+    dep = torch.empty_like(vs.flat_depth); pos = torch.empty_like(vs.position); msk = torch.empty_like(vs.mask)
+    static_us = _graph_us(lambda: eb.eagle_tree_mask_static(w.batch, w.T, fpd, vs.ctx_len, dep, pos, msk), reps)
+
+    def decode_step():
+        vs.tree()
+        vs.rope()
+        vs.attention()
+        vs.verify(temperature, seed, 0)
+        vs.commit()
+    decode_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        decode_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    full_us = e0.elapsed_time(e1) * 1e3 / 10
+    return {
+        "rope": {"us_per_layer_call": round(rope_us, 3), "bytes_per_call": rope_bytes,
+                 "GBps": round(rope_bytes / (rope_us * 1e-6) / 1e9, 1),
+                 "what": "q and the K tree rows of one layer rotated in place at their tree positions"},
+        "kv_commit": {"us_per_call": round(commit_us, 3), "accept_len": [int(x) for x in al],
+                      "rows_moved": moved, "bytes_per_call": commit_bytes,
+                      "GBps": round(commit_bytes / (commit_us * 1e-6) / 1e9, 1) if commit_bytes else None,
+                      "what": f"K and V of the accepted rows moved behind the context in all {vs.n_layers} "
+                              f"layers (path: the deepest root path of the tree)"},
+        "mask_static": {"us_per_call": round(static_us, 3)},
+        "timing": "graph replays of the calls, HIP events",
+        "decode_step_with_rope_and_commit": {
+            "ms": round(full_us / 1e3, 4), "steps_per_s": round(1e6 / full_us, 2),
+            "what": "expand x depth + rerank + mask + (rotary + attention) x layers + verify + KV commit, "
+                    "eager launches"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +184,7 @@ def main():
     ap.add_argument("--config", default="llama2_13b")
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip timing rotary, KV commit and the static mask")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 3 times (a plain copy kernel of "
                          "known size whose FETCH_SIZE / WRITE_SIZE counters scale the attention's)")
@@ -176,6 +267,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms_per_launch = e0.elapsed_time(e1) / (5 * n_attn)
+    # calls around the step, timed after it (they rewrite q and the K/V caches in place)
+    extras = None if args.no_extras or graph is not None else time_extras(vs, w, stream, temperature, seed)
     if args.copy_calibration > 0:
         nbytes = args.copy_calibration << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -229,6 +322,8 @@ def main():
             "us_per_launch": round(ms_per_launch * 1e3, 3),
         },
     }
+    if extras is not None:
+        out["around_step"] = extras
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (bounded sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, vs.draft_np, vs.root_np, target, temperature, seed)

@@ -3,6 +3,7 @@
 // commit of the accepted path.  All three are small (tens of KB to a few MB per
 // step) and latency-bound; each is one launch.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "launchers.hpp"
@@ -52,11 +53,16 @@ __global__ __launch_bounds__(64) void mask_static_kernel(int T, const int32_t* _
 
 // ---------------------------------------------------------------------------
 // Rotary position encoding of the tree rows.  One workgroup per (tree row,
-// sequence): the row's head_dim/2 cosines and sines (fp64) go to LDS, then the
-// workgroup rotates the row's query heads and its KV heads' tree row in place.
-// Consecutive threads take consecutive coordinates of a head, so every load and
-// store of a head row is one coalesced sweep.
+// sequence, slice of kRopeHeads heads), the query heads of the row followed by
+// the KV heads' tree row.  Thread t takes coordinate pair d = t mod (D/2) of every
+// (256 / (D/2))-th head of the slice: it computes the pair's angle, cosine and
+// sine once (fp64) and rotates that pair in each of its heads; consecutive threads
+// take consecutive coordinates, so each head row is read and written in
+// coalesced sweeps.  The frequencies base^(-2d/D) arrive as launch arguments,
+// computed once on the host.
 // ---------------------------------------------------------------------------
+constexpr int kRopeHeads = 16;
+
 __device__ __forceinline__ double load_elt(const float* p) { return (double)*p; }
 __device__ __forceinline__ double load_elt(const uint16_t* p) {
     return (double)__uint_as_float((uint32_t)*p << 16);
@@ -72,44 +78,61 @@ __device__ __forceinline__ void store_elt(uint16_t* p, double x) {
     *p = (uint16_t)(u >> 16);
 }
 
-template <typename Elt>
-__device__ __forceinline__ void rotate_pair(Elt* row, int d, int half, double c, double s) {
-    const double x = load_elt(row + d), y = load_elt(row + d + half);
-    store_elt(row + d, x * c - y * s);
-    store_elt(row + d + half, y * c + x * s);
-}
+constexpr int kRopeHostRows = 32;  // sequences whose K row may ride in the launch arguments
 
-template <typename Elt>
+struct RopeArgs {
+    double f[128];                     // base^(-2d/D), d < D/2
+    int64_t k_row0[kRopeHostRows];     // kv_row_off[b] + ctx_len[b], when the host has them
+};
+
+// Every load a thread needs is issued before it waits for any: the position of
+// its row and both halves of its coordinate pair in each of its heads, so one
+// memory round trip covers the kernel.
+template <typename Elt, bool HOST_ROWS>
 __global__ __launch_bounds__(256) void rope_kernel(int T, int Hq, int Hkv, int D,
                                                    const int32_t* __restrict__ position,
                                                    const int32_t* __restrict__ ctx_len,
                                                    const int64_t* __restrict__ kv_row_off,
-                                                   int64_t kv_rows_total, double base, Elt* q, Elt* k) {
-    __shared__ double cs[128], sn[128];
+                                                   int64_t kv_rows_total, RopeArgs ra, Elt* q, Elt* k) {
+    constexpr int kMaxPer = kRopeHeads / 2;  // groups >= 2 since D/2 <= 128
     const int i = blockIdx.x, b = blockIdx.y;
     const int half = D >> 1;
-    const double p = (double)position[(size_t)b * T + i];
-    for (int d = threadIdx.x; d < half; d += blockDim.x) {
-        const double theta = p * pow(base, -2.0 * d / D);
-        double s, c;
-        sincos(theta, &s, &c);
-        cs[d] = c;
-        sn[d] = s;
+    const int groups = blockDim.x / half;
+    const int d = threadIdx.x % half, grp = threadIdx.x / half;
+    if (grp >= groups) return;
+    const int nq = q ? Hq : 0;
+    const int h0 = blockIdx.z * kRopeHeads;
+    const int h_end = min(h0 + kRopeHeads, nq + (k ? Hkv : 0));
+    int64_t krow = -1;
+    if (k && h_end > nq) {
+        krow = HOST_ROWS ? ra.k_row0[b] + i : kv_row_off[b] + (int64_t)ctx_len[b] + i;
+        if (krow < 0 || krow >= kv_rows_total) krow = -1;  // outside the cache: K is not rotated
     }
-    __syncthreads();
-    if (q) {
-        Elt* qr = q + ((size_t)b * T + i) * (size_t)Hq * D;
-        for (int e = threadIdx.x; e < Hq * half; e += blockDim.x) {
-            const int h = e / half, d = e - h * half;
-            rotate_pair(qr + (size_t)h * D, d, half, cs[d], sn[d]);
+    const int32_t pos = position[(size_t)b * T + i];
+    Elt* rows[kMaxPer];
+    double x[kMaxPer], y[kMaxPer];
+#pragma unroll
+    for (int s = 0; s < kMaxPer; ++s) {
+        const int h = h0 + grp + s * groups;
+        rows[s] = nullptr;
+        if (h < h_end) {
+            if (h < nq)
+                rows[s] = q + (((size_t)b * T + i) * Hq + h) * D;
+            else if (krow >= 0)
+                rows[s] = k + ((size_t)(h - nq) * kv_rows_total + krow) * D;
+        }
+        if (rows[s]) {
+            x[s] = load_elt(rows[s] + d);
+            y[s] = load_elt(rows[s] + d + half);
         }
     }
-    if (k) {
-        const int64_t row = kv_row_off[b] + (int64_t)ctx_len[b] + i;
-        if (row < 0 || row >= kv_rows_total) return;  // outside the cache: nothing to rotate
-        for (int e = threadIdx.x; e < Hkv * half; e += blockDim.x) {
-            const int h = e / half, d = e - h * half;
-            rotate_pair(k + ((size_t)h * kv_rows_total + row) * D, d, half, cs[d], sn[d]);
+    double sn, cs;
+    sincos((double)pos * ra.f[d], &sn, &cs);
+#pragma unroll
+    for (int s = 0; s < kMaxPer; ++s) {
+        if (rows[s]) {
+            store_elt(rows[s] + d, x[s] * cs - y[s] * sn);
+            store_elt(rows[s] + d + half, y[s] * cs + x[s] * sn);
         }
     }
 }
@@ -199,15 +222,23 @@ hipError_t launch_mask_static(int batch, int T, const int32_t* flat_parent, cons
 
 hipError_t launch_rope(const eagle_attn_desc& d, const int32_t* position, double base, void* q, void* k,
                        hipStream_t stream) {
-    const dim3 grid(d.T, d.batch);
-    if (d.dtype == EAGLE_BF16)
-        rope_kernel<uint16_t><<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position,
-                                                         d.ctx_len, d.kv_row_off, d.kv_rows_total, base,
-                                                         (uint16_t*)q, (uint16_t*)k);
-    else
-        rope_kernel<float><<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position,
-                                                      d.ctx_len, d.kv_row_off, d.kv_rows_total, base,
-                                                      (float*)q, (float*)k);
+    RopeArgs ra{};
+    const int half = d.head_dim / 2;
+    for (int j = 0; j < half; ++j) ra.f[j] = pow(base, -2.0 * j / d.head_dim);
+    const bool host_rows = d.ctx_len_host && d.kv_row_off_host && d.batch <= kRopeHostRows;
+    if (host_rows)
+        for (int b = 0; b < d.batch; ++b) ra.k_row0[b] = d.kv_row_off_host[b] + d.ctx_len_host[b];
+    const int heads = (q ? d.n_q_heads : 0) + (k ? d.n_kv_heads : 0);
+    const dim3 grid(d.T, d.batch, (heads + kRopeHeads - 1) / kRopeHeads);
+    if (d.dtype == EAGLE_BF16) {
+        auto kern = host_rows ? rope_kernel<uint16_t, true> : rope_kernel<uint16_t, false>;
+        kern<<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position, d.ctx_len,
+                                       d.kv_row_off, d.kv_rows_total, ra, (uint16_t*)q, (uint16_t*)k);
+    } else {
+        auto kern = host_rows ? rope_kernel<float, true> : rope_kernel<float, false>;
+        kern<<<grid, 256, 0, stream>>>(d.T, d.n_q_heads, d.n_kv_heads, d.head_dim, position, d.ctx_len,
+                                       d.kv_row_off, d.kv_rows_total, ra, (float*)q, (float*)k);
+    }
     return hipGetLastError();
 }
 

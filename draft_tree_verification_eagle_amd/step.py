@@ -102,6 +102,24 @@ class VerifyStep:
         eb.eagle_verify(self.cfg, self.target, self.flat_token, self.flat_parent, temperature, seed, step,
                         self.accept_len, self.accept_path, self.out_tokens, self.verify_ws, stream)
 
+    def rope(self, layers: Optional[Sequence[int]] = None, base: float = 10000.0, stream=None):
+        """Rotary at the tree positions, in place on each layer's q and K tree rows."""
+        for layer in (range(self.n_layers) if layers is None else layers):
+            a = self.attn[layer]
+            eb.eagle_tree_rope(self.desc, self.position, base, a["q"], a["k"], stream)
+
+    def commit(self, stream=None):
+        """Move the accepted rows' K/V of every layer behind the context
+        (accept_len / accept_path from the last verify)."""
+        if not hasattr(self, "new_ctx_len"):
+            self.new_ctx_len = torch.zeros_like(self.ctx_len)
+            dtype = eb.EAGLE_F32 if self.w.dtype == "f32" else eb.EAGLE_BF16
+            self.commit_desc = eb.make_commit_desc(dtype, self.w.batch, self.w.T, self.w.depth, self.w.n_kv_heads,
+                                                   self.w.head_dim, self.n_layers, self.ctx_len, self.kv_row_off,
+                                                   self.kv_rows_total)
+        eb.eagle_kv_commit(self.commit_desc, self.accept_len, self.accept_path, [a["k"] for a in self.attn],
+                           [a["v"] for a in self.attn], self.new_ctx_len, stream)
+
     def run(self, temperature: float, seed: int, step: int, stream=None):
         self.tree(stream)
         self.attention(stream=stream)

@@ -240,8 +240,11 @@ int eagle_tree_mask_static(int32_t batch, int32_t T, const int32_t* flat_parent,
  * Angles, cosines, sines and the rotation are fp64; the result is rounded to
  * fp32 (nearest even) and, for BF16, then to bf16 (nearest even).  Context rows
  * are not touched (the cache holds them already rotated).  desc as for
- * eagle_tree_attention (scale and the host copies unused); q or k_cache may be
- * NULL to rotate only the other.  head_dim even and <= 256, base > 0 and
+ * eagle_tree_attention (scale unused); when it carries host copies of ctx_len and
+ * kv_row_off and batch <= 32, each sequence's first tree row rides in the launch
+ * arguments (the copies must match the device arrays); otherwise the kernel reads
+ * the device arrays.  A tree row outside the cache is left alone.  q or k_cache
+ * may be NULL to rotate only the other.  head_dim even and <= 256, base > 0 and
  * finite.  Positions are not checked: p < 0 rotates backwards. */
 int eagle_tree_rope(const eagle_attn_desc* desc, const int32_t* position, double base, void* q,
                     void* k_cache, hipStream_t stream);

@@ -245,6 +245,23 @@ def test_rope_q_only_and_k_only(lib, orc):
     rope_check(eb, orc, vs, rotate_q=False)
 
 
+def test_rope_device_lengths_same_bits(lib, orc):
+    """Without host copies of the lengths the kernel reads the device arrays; the
+    bits are the same as with the rows passed as launch arguments."""
+    eb, stepm, wl = lib
+    w = small(wl, batch=3, ctx_range=(0, 900), n_q_heads=8, n_kv_heads=4, seed=21)
+    say("[rope] device-array lengths vs launch-argument rows")
+    outs = []
+    for host in (True, False):
+        vs = stepm.VerifyStep(w, layers=1, host_lengths=host)
+        vs.tree()
+        a = vs.attn[0]
+        eb.eagle_tree_rope(vs.desc, vs.position, 10000.0, a["q"], a["k"])
+        torch.cuda.synchronize()
+        outs.append((a["q"].clone(), a["k"].clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 # ---------------------------------------------------------------------------
 # KV commit of the accepted path
 # ---------------------------------------------------------------------------
