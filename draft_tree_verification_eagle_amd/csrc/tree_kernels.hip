@@ -336,27 +336,81 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// K3: per sequence, all non-root nodes sorted by (value desc, depth asc, id asc)
-// with one LDS bitonic sort; the first n ids are sorted again ascending.
+// K3: per sequence, the n first non-root nodes in (value desc, depth asc, id asc),
+// written in ascending id.  Node keys pack the three into one unique 64-bit
+// value, larger = earlier.  Up to kRankMax candidates (one per thread): a node's
+// rank is the number of larger keys (threads sweep the keys' value words in LDS,
+// four per broadcast read, and the full keys only where value words tie), the
+// node is kept iff rank < n, and its output slot is the number of kept nodes with
+// a smaller id (a block prefix count of ballots).  Larger trees: one LDS bitonic sort, then the n first ids sorted
+// again ascending.
 // ---------------------------------------------------------------------------
+constexpr int kRankMax = 1024;  // a multiple of 16, at most EAGLE_MAX_CAPACITY / 2
+static_assert(kRankMax % 16 == 0 && 2 * kRankMax <= EAGLE_MAX_CAPACITY, "rank path layout");
+
+__device__ __forceinline__ uint64_t rerank_key(const float* value, const int32_t* depth, int b, int cap, int id) {
+    const uint32_t dep = (uint32_t)depth[(size_t)b * cap + id];
+    return ((uint64_t)float_order_key(value[(size_t)b * cap + id]) << 32) | ((uint64_t)(255u - dep) << 24) |
+           (uint64_t)(0xFFFFFFu - (uint32_t)id);
+}
+
 __global__ __launch_bounds__(1024) void rerank_kernel(int cap, int n, const float* __restrict__ value,
                                                        const int32_t* __restrict__ depth,
                                                        int32_t* __restrict__ kept) {
-    __shared__ uint64_t keys[EAGLE_MAX_CAPACITY];
+    __shared__ __attribute__((aligned(16))) uint64_t keys[EAGLE_MAX_CAPACITY];
     __shared__ uint64_t sel[EAGLE_MAX_TREE_ROWS];
+    __shared__ int s_wave_kept[1024 / kWave];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int N = cap - 1;
-    const int P = next_pow2(N);
-    for (int i = tid; i < P; i += blockDim.x) {
-        uint64_t key = 0;
-        if (i < N) {
-            const uint32_t id = (uint32_t)(i + 1);
-            const uint32_t dep = (uint32_t)depth[(size_t)b * cap + id];
-            key = ((uint64_t)float_order_key(value[(size_t)b * cap + id]) << 32) |
-                  ((uint64_t)(255u - dep) << 24) | (uint64_t)(0xFFFFFFu - id);
+    if (N <= kRankMax) {
+        // hi[j]: the value word of node j + 1's key (its top 32 bits).  A sweep reads
+        // four of them per broadcast read: rank = #(larger value words) + #(equal value
+        // words with a larger full key).  Only waves holding keys sweep, and the full
+        // keys are swept only by a wave in which some node's value word is not unique.
+        uint32_t* hi = reinterpret_cast<uint32_t*>(keys + kRankMax);  // past the keys: N16 <= kRankMax
+        const int lane = tid & (kWave - 1), wid = tid / kWave;
+        const int N16 = (N + 15) & ~15;
+        const uint64_t mine = tid < N ? rerank_key(value, depth, b, cap, tid + 1) : 0;
+        for (int j = tid; j < N16; j += blockDim.x) {
+            const uint64_t kj = j == tid ? mine : 0;  // pads: key 0, value word 0
+            keys[j] = kj;
+            hi[j] = (uint32_t)(kj >> 32);
         }
-        keys[i] = key;
+        __syncthreads();
+        int rank = 0;
+        if (wid * kWave < N) {
+            const uint32_t h = (uint32_t)(mine >> 32);
+            int eq = 0;  // nodes with the same value word, this one included
+            for (int j = 0; j < N16; j += 16) {
+                uint4 hh[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) hh[u] = *reinterpret_cast<const uint4*>(&hi[j + 4 * u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    rank += (hh[u].x > h) + (hh[u].y > h) + (hh[u].z > h) + (hh[u].w > h);
+                    eq += (hh[u].x == h) + (hh[u].y == h) + (hh[u].z == h) + (hh[u].w == h);
+                }
+            }
+            if (__any(tid < N && eq > 1)) {
+                int tie = 0;
+                for (int j = 0; j < N16; j += 2) {
+                    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&keys[j]);
+                    tie += ((uint32_t)(kk.x >> 32) == h && kk.x > mine) + ((uint32_t)(kk.y >> 32) == h && kk.y > mine);
+                }
+                rank += tie;
+            }
+        }
+        const bool keep = tid < N && rank < n;
+        const uint64_t bal = __ballot(keep);
+        if (lane == 0) s_wave_kept[wid] = __popcll(bal);
+        __syncthreads();
+        int before = __popcll(bal & ((1ull << lane) - 1ull));
+        for (int w = 0; w < wid; ++w) before += s_wave_kept[w];
+        if (keep) kept[(size_t)b * n + before] = tid + 1;
+        return;
     }
+    const int P = next_pow2(N);
+    for (int i = tid; i < P; i += blockDim.x) keys[i] = i < N ? rerank_key(value, depth, b, cap, i + 1) : 0;
     __syncthreads();
     lds_bitonic_sort_desc(keys, P);
     const int P2 = next_pow2(n > 0 ? n : 1);
@@ -375,9 +429,9 @@ __global__ __launch_bounds__(1024) void rerank_kernel(int cap, int n, const floa
 }
 
 // ---------------------------------------------------------------------------
-// K4: one wave per sequence; lane i owns flattened row i.  Parent rows are found
-// among the (ascending) kept ids; the ancestor mask is built by walking parent
-// rows, at most T steps.
+// K4: one wave per sequence; lane i owns flattened row i.  Parent rows come from
+// a node -> row table in LDS; the ancestor mask is built by walking parent rows,
+// at most T steps.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void mask_kernel(int cap, int n, const int32_t* __restrict__ token,
                                                    const int32_t* __restrict__ parent,
@@ -391,19 +445,23 @@ __global__ __launch_bounds__(64) void mask_kernel(int cap, int n, const int32_t*
                                                    uint64_t* __restrict__ mask) {
     __shared__ int32_t fnode[EAGLE_MAX_TREE_ROWS];
     __shared__ int32_t fpar[EAGLE_MAX_TREE_ROWS];
+    __shared__ int16_t row_of[EAGLE_MAX_CAPACITY];  // node -> flattened row, kept nodes only
     const int b = blockIdx.x, i = threadIdx.x;
     const int T = n + 1;
-    if (i < T) fnode[i] = (i == 0) ? 0 : kept[(size_t)b * n + (i - 1)];
-    __syncthreads();
-    int node = 0;
+    int node = 0, p = -1;
     if (i < T) {
-        node = fnode[i];
-        const int p = parent[(size_t)b * cap + node];
-        int pr = -1;
-        if (p >= 0) {
-            for (int r = 0; r < T; ++r)
-                if (fnode[r] == p) { pr = r; break; }
-        }
+        node = (i == 0) ? 0 : kept[(size_t)b * n + (i - 1)];
+        if (node < 0 || node >= cap) node = 0;  // not a node id: memory-safe, result unspecified
+        p = parent[(size_t)b * cap + node];
+        fnode[i] = node;
+        row_of[node] = (int16_t)i;
+    }
+    __syncthreads();
+    // The kept set is ancestor-closed, so a kept node's parent has its entry; the
+    // entry is checked against the row's node so a stale one reads as no parent.
+    if (i < T) {
+        int pr = p >= 0 && p < cap ? row_of[p] : -1;
+        if (pr < 0 || pr >= T || fnode[pr] != p) pr = -1;
         fpar[i] = pr;
     }
     __syncthreads();

@@ -11,7 +11,7 @@
 // p(tok) / (mass of tokens not yet rejected at this row); rejected tokens are
 // removed; the bonus token is drawn from the remaining mass by inverse CDF.
 //
-// K6 (one workgroup per row) computes argmax, row max and, for sampling, the fp64
+// K6 (four workgroups per row) computes argmax, row max and, for sampling, the fp64
 // masses exp((z - zmax) / temperature) of every child token plus the fp64 mass of
 // all other tokens, summed directly (never as 1 - sum of removed), and the
 // fixed-point mass of each of 1024 contiguous token chunks.  K7 (one workgroup
@@ -41,7 +41,7 @@ __device__ __forceinline__ uint64_t fixed_mass(double e, double scale) { return 
 
 // Per-row statistics in the workspace.
 struct RowStats {
-    double rest;        // mass of tokens that are not children of the row
+    double rest[4];     // mass of tokens that are not children of the row, per quarter of its chunks
     double kid_e[kKids];  // mass of each child's token, flattened order
     int32_t kid_row[kKids];
     float zmax;
@@ -51,18 +51,26 @@ struct RowStats {
 };
 
 // ---------------------------------------------------------------------------
-// K6: one workgroup of 1024 threads per (row, sequence).  Wave 0 finds the row's
-// children with one ballot (flattened order = lane order).  The argmax pass reads
-// token t = tid + 1024 * it (coalesced); the mass pass gives thread tid the
-// contiguous chunk [tid * ch, tid * ch + ch), ch = ceil(V / 1024) <= 256 (re-read,
-// from L2), with a 256-bit mask of the children in it, and stores the chunk's
-// fixed-point mass (children included) for the bonus draw.
+// K6: kRowSplit workgroups of 256 threads per (row, sequence), all four on one
+// XCD (blockIdx.x mod 8) so the row is fetched from HBM once and re-read from
+// that XCD's L2.  Every workgroup finds the row's maximum and argmax over the
+// whole row (float4 loads, all in flight together for vocabularies up to 32768);
+// then, for sampling, workgroup q takes chunks [256 q, 256 q + 256) of the row's
+// 1024 contiguous token chunks (ch = ceil(V / 1024) tokens each; thread = chunk,
+// re-read from L2), with a 256-bit mask of the row's children in the chunk: it
+// stores each chunk's fixed-point mass (children included) for the bonus draw and
+// the fp64 mass of the non-child tokens of its quarter.  Workgroup 0 also writes
+// the children, their fp64 masses, the argmax and the maximum.  Wave 0 of each
+// workgroup finds the children with one ballot (flattened order = lane order).
 // ---------------------------------------------------------------------------
-constexpr int kRowThreads = 1024;
+constexpr int kRowSplit = 4;
+constexpr int kRowThreads = 256;
+constexpr int kRowChunks = kRowSplit * kRowThreads;  // 1024 chunks per row
 constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kRowBatch = 32;       // tokens per thread loaded together
+constexpr int kRowBatch = 32;       // loads per thread in flight together
 constexpr int kMaxChunkTokens = 256;  // ceil(EAGLE_MAX_VOCAB / 1024)
-static_assert((EAGLE_MAX_VOCAB + kRowThreads - 1) / kRowThreads <= kMaxChunkTokens, "chunk mask");
+static_assert((EAGLE_MAX_VOCAB + kRowChunks - 1) / kRowChunks <= kMaxChunkTokens, "chunk mask");
+static_assert(kRowSplit == 4, "RowStats keeps four partial rest masses");
 
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     const float* __restrict__ target, int T, int V, const int32_t* __restrict__ flat_token,
@@ -73,7 +81,11 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     __shared__ int s_nk;
     __shared__ uint64_t s_key[kRowWaves];
     __shared__ double s_red[kRowWaves];
-    const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    // blockIdx.x = 8 * (kRowSplit * (i / 8) + q) + i % 8: the quarters of row i share an XCD
+    const int xb = blockIdx.x;
+    const int i = 8 * (xb / (8 * kRowSplit)) + (xb & 7), q = (xb >> 3) % kRowSplit;
+    const int b = blockIdx.y, tid = threadIdx.x;
+    if (i >= T || (q > 0 && !(temperature > 0.0f))) return;  // greedy needs the argmax only
     const int lane = tid & (kWave - 1), wid = tid / kWave;
     const float* z = target + ((size_t)b * T + i) * (size_t)V;
     if (wid == 0) {
@@ -86,24 +98,48 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         }
         if (lane == 0) s_nk = __popcll(bal) < kKids ? __popcll(bal) : kKids;
     }
-    // Thread tid reads tokens t = tid + 1024 * it in unrolled batches of 32 (all
-    // loads of a batch in flight together); with vocab <= 32768 the single batch
-    // stays in registers for the second pass.
-    const int iters = (V + kRowThreads - 1) / kRowThreads;  // <= 256
-    float zr[kRowBatch];
+    // maximum and argmax over the whole row: (logit, ~token) keys, order-free
     uint64_t best = 0;
-    for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
+    const bool vec = (V & 3) == 0 && ((uintptr_t)target & 15) == 0;
+    if (vec) {
+        const int n4 = V >> 2;
+        const float4* z4 = reinterpret_cast<const float4*>(z);
+        for (int j0 = 0; j0 < n4; j0 += kRowBatch * kRowThreads) {
+            float4 zr[kRowBatch];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q) {
-            const int t = (it0 + q) * kRowThreads + tid;
-            zr[q] = t < V ? z[t] : 0.0f;
+            for (int u = 0; u < kRowBatch; ++u) {
+                const int j = j0 + u * kRowThreads + tid;
+                zr[u] = j < n4 ? z4[j] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < kRowBatch; ++u) {
+                const int j = j0 + u * kRowThreads + tid;
+                if (j < n4) {
+                    const uint32_t t = 4u * (uint32_t)j;
+                    uint64_t k0 = logit_key(zr[u].x, t), k1 = logit_key(zr[u].y, t + 1);
+                    uint64_t k2 = logit_key(zr[u].z, t + 2), k3 = logit_key(zr[u].w, t + 3);
+                    k0 = k1 > k0 ? k1 : k0;
+                    k2 = k3 > k2 ? k3 : k2;
+                    k0 = k2 > k0 ? k2 : k0;
+                    best = k0 > best ? k0 : best;
+                }
+            }
         }
+    } else {
+        for (int t0 = 0; t0 < V; t0 += kRowBatch * kRowThreads) {
+            float zr[kRowBatch];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q) {
-            const int t = (it0 + q) * kRowThreads + tid;
-            if (t < V) {
-                const uint64_t key = logit_key(zr[q], (uint32_t)t);
-                best = key > best ? key : best;
+            for (int u = 0; u < kRowBatch; ++u) {
+                const int t = t0 + u * kRowThreads + tid;
+                zr[u] = t < V ? z[t] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kRowBatch; ++u) {
+                const int t = t0 + u * kRowThreads + tid;
+                if (t < V) {
+                    const uint64_t key = logit_key(zr[u], (uint32_t)t);
+                    best = key > best ? key : best;
+                }
             }
         }
     }
@@ -119,8 +155,9 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         const double temp = (double)temperature;
         const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
         const double fscale = ldexp(1.0, fixed_shift(V));
-        const int ch = (V + kRowThreads - 1) / kRowThreads;
-        const int c0 = min(V, tid * ch), c1 = min(V, c0 + ch);
+        const int ch = (V + kRowChunks - 1) / kRowChunks;
+        const int chunk = q * kRowThreads + tid;
+        const int c0 = min(V, chunk * ch), c1 = min(V, c0 + ch);
         uint64_t km[4] = {0, 0, 0, 0};  // bit d: token c0 + d is a child of the row
         for (int c = 0; c < nk; ++c) {
             const int d = s_kid_tok[c] - c0;
@@ -133,19 +170,19 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         double s = 0.0;
         uint64_t fm = 0;
         // 16-byte aligned chunk starts: vector loads
-        const bool vec = (V & 3) == 0 && (ch & 3) == 0 && ((uintptr_t)target & 15) == 0;
+        const bool cvec = vec && (ch & 3) == 0;
         for (int a0 = c0; a0 < c1; a0 += kRowBatch) {
             float zz[kRowBatch];
-            if (vec) {
+            if (cvec) {
 #pragma unroll
-                for (int q = 0; q < kRowBatch; q += 4) {
+                for (int u = 0; u < kRowBatch; u += 4) {
                     float4 v4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (a0 + q < c1) v4 = *reinterpret_cast<const float4*>(z + a0 + q);
-                    zz[q] = v4.x; zz[q + 1] = v4.y; zz[q + 2] = v4.z; zz[q + 3] = v4.w;
+                    if (a0 + u < c1) v4 = *reinterpret_cast<const float4*>(z + a0 + u);
+                    zz[u] = v4.x; zz[u + 1] = v4.y; zz[u + 2] = v4.z; zz[u + 3] = v4.w;
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < kRowBatch; ++q) zz[q] = a0 + q < c1 ? z[a0 + q] : 0.0f;
+                for (int u = 0; u < kRowBatch; ++u) zz[u] = a0 + u < c1 ? z[a0 + u] : 0.0f;
             }
             const int o = a0 - c0;  // a multiple of 32: bits o .. o + 31 of the mask
             uint64_t kw = km[0];
@@ -154,20 +191,22 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
                 if ((o >> 6) == w) kw = km[w];
             const uint32_t kb = (uint32_t)(kw >> (o & 63));
 #pragma unroll
-            for (int q = 0; q < kRowBatch; ++q) {
-                if (a0 + q < c1) {
-                    const double x = (double)zz[q] - (double)zmax;
+            for (int u = 0; u < kRowBatch; ++u) {
+                if (a0 + u < c1) {
+                    const double x = (double)zz[u] - (double)zmax;
                     const double e = exp_nonpos_f64(unit_temp ? x : x / temp);
                     fm += fixed_mass(e, fscale);
-                    if (!((kb >> q) & 1u)) s += e;
+                    if (!((kb >> u) & 1u)) s += e;
                 }
             }
         }
-        chunk_mass[((size_t)b * T + i) * kRowThreads + tid] = fm;
+        chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
         s = block_sum_f64(s, s_red);
-        if (tid < nk) out->kid_e[tid] = exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
-        if (tid == 0) out->rest = s;
+        if (tid == 0) out->rest[q] = s;
+        if (q == 0 && tid < nk)
+            out->kid_e[tid] = exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
     }
+    if (q != 0) return;
     if (tid < nk) out->kid_row[tid] = s_kid_row[tid];
     if (tid == 0) {
         out->zmax = zmax;
@@ -180,7 +219,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
 // K7
 // ---------------------------------------------------------------------------
 constexpr int kWalkThreads = 1024;
-static_assert(kWalkThreads == kRowThreads, "one chunk mass per walk thread");
+static_assert(kWalkThreads == kRowChunks, "one chunk mass per walk thread");
 constexpr int kMaxDepth = 255;  // the library's depth limit
 
 // Exclusive block prefix sum of one uint64 per thread (exact, order-free);
@@ -257,7 +296,7 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                     if (!sampled) {
                         pass = s_tok[R.kid_row[lane]] == R.argmax;
                     } else {
-                        double denom = R.rest;
+                        double denom = ((R.rest[0] + R.rest[1]) + R.rest[2]) + R.rest[3];
                         for (int c = lane; c < nk; ++c) denom += R.kid_e[c];
                         const double ratio = R.kid_e[lane] / denom;
                         const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)lane);
@@ -370,7 +409,7 @@ static size_t stats_bytes(const eagle_tree_cfg& cfg) {
     return ((size_t)cfg.batch * (size_t)(cfg.n + 1) * sizeof(RowStats) + 255) & ~(size_t)255;
 }
 size_t verify_workspace_bytes(const eagle_tree_cfg& cfg) {
-    return stats_bytes(cfg) + (size_t)cfg.batch * (size_t)(cfg.n + 1) * kRowThreads * sizeof(uint64_t);
+    return stats_bytes(cfg) + (size_t)cfg.batch * (size_t)(cfg.n + 1) * kRowChunks * sizeof(uint64_t);
 }
 
 hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const int32_t* flat_token,
@@ -380,7 +419,9 @@ hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const i
     const int T = cfg.n + 1;
     RowStats* stats = (RowStats*)workspace;
     uint64_t* chunk_mass = (uint64_t*)((unsigned char*)workspace + stats_bytes(cfg));
-    verify_rows_kernel<<<dim3(T, cfg.batch), kRowThreads, 0, stream>>>(
+    // rows padded to a multiple of 8 so the quarters of a row share an XCD
+    const int row_groups = (T + 7) / 8;
+    verify_rows_kernel<<<dim3(8 * kRowSplit * row_groups, cfg.batch), kRowThreads, 0, stream>>>(
         target, T, cfg.vocab, flat_token, flat_parent, temperature, stats, chunk_mass);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -367,3 +367,31 @@ def test_branch_independence_on_gpu(lib, orc):
             assert same != sees, f"row {i} vs perturbed tree row {j}"
         a["k"][:, ctx + j] = k_keep
         a["v"][:, ctx + j] = v_keep
+
+
+@pytest.mark.parametrize("depth,topk,m,n,levels", [(6, 10, 10, 60, 3), (6, 10, 10, 60, 40), (2, 32, 32, 63, 5),
+                                                   (4, 4, 4, 15, 1)],
+                         ids=["511-nodes-3-values", "511-nodes-40-values", "1057-nodes-5-values", "53-nodes-1-value"])
+def test_rerank_ties_crafted_states(lib, orc, depth, topk, m, n, levels):
+    """Rerank on tree states whose values take a few levels only, so most keys tie
+    on value and the depth and id tie-breaks decide (the rank path up to 1024
+    candidates, the sort path above)."""
+    eb, stepm, wl = lib
+    B = 3
+    cfg = eb.make_cfg(B, 100, depth, topk, m, n)
+    cap = eb.eagle_tree_capacity(cfg)
+    say(f"[rerank ties] {cap} nodes, {levels} value levels")
+    st = eb.TreeState.allocate(cfg, "cuda")
+    rng = np.random.default_rng(cap + levels)
+    vals = np.zeros((B, cap), np.float32); deps = np.zeros((B, cap), np.int32)
+    for b in range(B):
+        lv = -np.sort(rng.random(levels).astype(np.float32) * 8.0)
+        vals[b, 1:] = rng.choice(lv, cap - 1)
+        deps[b, 1:] = rng.integers(1, depth + 1, cap - 1)
+    st.value.copy_(torch.from_numpy(vals)); st.depth.copy_(torch.from_numpy(deps))
+    kept = torch.full((B, n), -7, dtype=torch.int32, device="cuda")
+    eb.eagle_tree_rerank(cfg, st, kept)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    for b in range(B):
+        np.testing.assert_array_equal(got[b], orc.rerank(vals[b], deps[b], n))
