@@ -262,6 +262,49 @@ def test_attention_parity_batched_ragged_sampled(lib, orc):
     assert torch.isfinite(vs.attn[0]["o"].float()).all()
 
 
+def test_attention_parity_batched_sequences_one_by_one(lib, orc):
+    """The batched workload's attention at full size, one sequence per call: each of
+    the 16 ragged sequences (contexts 512-16384) gets its own batch-1 descriptor over
+    a contiguous copy of its K/V rows (the batched call also launches the kernels once
+    per sequence).  Sampled outputs of every sequence against the oracle."""
+    eb, stepm, wl = lib
+    w = wl.CONFIGS["batched_13b"]
+    say("[attention parity] batched_13b, 1 layer, each of the 16 sequences in its own call")
+    vs = stepm.VerifyStep(w, layers=0)
+    vs.tree()
+    torch.cuda.synchronize()
+    trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    q, k, v, off, total = wl.attention_inputs(w, 0, device="cuda", ctx_lens=vs.ctx_lens_np)
+    rng = np.random.default_rng(5)
+    order = np.argsort(vs.ctx_lens_np)
+    for b in [int(x) for x in order]:
+        ctx = int(vs.ctx_lens_np[b]); rows = ctx + w.T; r0 = int(off[b])
+        kb = k[:, r0:r0 + rows].contiguous(); vb = v[:, r0:r0 + rows].contiguous()
+        qb = q[b:b + 1].contiguous()
+        ctx_t = torch.tensor([ctx], dtype=torch.int32, device="cuda")
+        off_t = torch.zeros(1, dtype=torch.int64, device="cuda")
+        d = eb.make_attn_desc(eb.EAGLE_BF16, 1, w.T, w.n_q_heads, w.n_kv_heads, w.head_dim, ctx_t, off_t, rows,
+                              ctx_len_host=[ctx], kv_row_off_host=[0])
+        ws = torch.zeros(max(eb.eagle_tree_attention_workspace(d), 1), dtype=torch.uint8, device="cuda")
+        o = torch.full_like(qb, float("nan"))
+        lse = torch.full((1, w.T, w.n_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+        say(f"  sequence {b}: ctx {ctx}")
+        eb.eagle_tree_attention(d, qb, kb, vb, vs.mask[b:b + 1].contiguous(), o, lse, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all()
+        sel = [(int(i), int(h)) for i, h in zip(rng.integers(0, w.T, 24), rng.integers(0, w.n_q_heads, 24))]
+        sel += [(0, 0), (w.T - 1, w.n_q_heads - 1)]
+        oo, ll = orc.attention(qb[0].float().cpu().numpy(), kb.float().cpu().numpy(), vb.float().cpu().numpy(),
+                               trees[b][2]["mask"], ctx, sel=sel)
+        og = o[0].float().cpu().numpy(); lg = lse[0].cpu().numpy()
+        got = np.stack([og[i, h] for i, h in sel])
+        err = np.abs(got - oo).max()
+        lerr = max(abs(lg[i, h] - ll[j]) for j, (i, h) in enumerate(sel))
+        assert err <= ATOL_BF16, f"sequence {b} (ctx {ctx}): max |o - oracle| = {err}"
+        assert lerr <= ATOL_BF16, f"sequence {b} (ctx {ctx}): max |lse - oracle| = {lerr}"
+        del kb, vb
+
+
 @pytest.mark.parametrize("name,temps", [("tiny_f32", (0.0,)), ("llama2_7b_layer", (0.0,)),
                                         ("llama2_13b", (1.0,)), ("llama2_70b_gqa", (0.0, 0.7)),
                                         ("batched_13b", (1.0,))])
