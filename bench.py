@@ -52,6 +52,20 @@ def attention_bytes_per_launch(w) -> int:
     return kv + qo
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # fp32 vector
+
+
+def attention_flops_per_launch(w, mask_words, ctx_lens) -> int:
+    """QK^T and PV multiply-adds over the keys each tree row attends to (its
+    context and its ancestors, itself included): 4 * D per (query head, key)."""
+    total = 0
+    for b in range(w.batch):
+        keys = sum(int(ctx_lens[b]) + bin(int(x) & (2**64 - 1)).count("1") for x in mask_words[b])
+        total += keys * w.n_q_heads * 4 * w.head_dim
+    return total
+
+
 def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 8):
     """Oracle timing on a bounded sample: full tree + `layers` distinct attention
     layers + one verification, single-threaded, scaled to the full step
@@ -279,6 +293,9 @@ def main():
         print(f"[bench] copy calibration: 3 x {nbytes} bytes", file=sys.stderr, flush=True)
     bytes_launch = attention_bytes_per_launch(w)
     achieved = bytes_launch / (ms_per_launch * 1e-3) / 1e9
+    flops_launch = attention_flops_per_launch(w, vs.mask.cpu().numpy(), vs.ctx_lens_np)
+    tflops = flops_launch / (ms_per_launch * 1e-3) / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         # counters taken on an older kernel source do not describe this one
@@ -320,6 +337,10 @@ def main():
             "kernel": "tree_attn_bf16_kernel + tree_attn_merge_kernel (one eagle_tree_attention call)",
             "bytes_per_launch": bytes_launch,
             "us_per_launch": round(ms_per_launch * 1e3, 3),
+            "flops_per_launch": flops_launch,
+            "mfma_side": {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": mfma_peak,
+                          "frac": round(tflops / mfma_peak, 4),
+                          "flop_per_byte": round(flops_launch / bytes_launch, 1)},
         },
     }
     if extras is not None:

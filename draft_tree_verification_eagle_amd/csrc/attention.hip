@@ -863,7 +863,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
 }
 
 // ---------------------------------------------------------------------------
-// FP32 path: one wave per (tree row, query head); lane = head dimension.
+// FP32 path: one wave per (tree row, query head).
 // ---------------------------------------------------------------------------
 struct AttnF32Args {
     const float* q;
@@ -879,39 +879,111 @@ struct AttnF32Args {
     float scale;
 };
 
-__global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnF32Args a) {
-    const int i = blockIdx.x, b = blockIdx.z;
+// One workgroup of four waves per (tree row, query head).  Keys in blocks of 64,
+// dealt to the waves in turn (block j to wave j mod 4), each wave running an online
+// softmax over its blocks: lane c scores key k0 + c in full (q broadcast from LDS),
+// one wave maximum and sum per block, then P V with lane = head dimension (two per
+// lane when D > 64), the block's probabilities taken from their lanes by readlane.
+// Invisible keys (tree rows off the row's root path) score -inf.  The four partial
+// (max, sum, output) are combined through LDS.
+constexpr int kF32Waves = 4;
+
+__global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Args a) {
+    __shared__ __attribute__((aligned(16))) float s_q[128];
+    __shared__ float s_ml[2][kF32Waves];
+    __shared__ float s_o[kF32Waves][128];
+    const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
     const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int hq = blockIdx.y * 4 + wid;
-    if (hq >= a.Hq) return;
     const int g = hq / a.G;
     const int ctx = a.ctx_len[b], S = ctx + a.T, D = a.D;
     const uint64_t mword = a.mask[(int64_t)b * a.T + i];
     const float* qrow = a.q + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
-    const float q0 = lane < D ? qrow[lane] : 0.0f;
-    const float q1 = lane + kWave < D ? qrow[lane + kWave] : 0.0f;
+    if (threadIdx.x < D) s_q[threadIdx.x] = qrow[threadIdx.x] * a.scale;
+    __syncthreads();
     const int64_t base = ((int64_t)g * a.kv_rows_total + a.kv_row_off[b]) * D;
     float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int c = 0; c < S; ++c) {
-        if (c >= ctx && !((mword >> (c - ctx)) & 1ull)) continue;
-        const float* kr = a.k + base + (int64_t)c * D;
-        const float* vr = a.v + base + (int64_t)c * D;
-        float part = 0.0f;
-        if (lane < D) part += q0 * kr[lane];
-        if (lane + kWave < D) part += q1 * kr[lane + kWave];
-        const float s = wave_sum_f32(part) * a.scale;
-        const float m_new = fmaxf(m, s);
-        const float alpha = expf(m - m_new);
-        const float p = expf(s - m_new);
-        l = l * alpha + p;
-        o0 = o0 * alpha + (lane < D ? p * vr[lane] : 0.0f);
-        o1 = o1 * alpha + (lane + kWave < D ? p * vr[lane + kWave] : 0.0f);
+    for (int k0 = wid * kWave; k0 < S; k0 += kF32Waves * kWave) {
+        const int c = k0 + lane;
+        const bool vis = c < S && (c < ctx || ((mword >> (c - ctx)) & 1ull));
+        float s = -INFINITY;
+        if (vis) {
+            const float* kr = a.k + base + (int64_t)c * D;
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if ((D & 3) == 0) {  // rows are 16-byte aligned: vector loads, eight in flight
+                for (int d0 = 0; d0 < D; d0 += 32) {
+                    float4 kv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        kv[u] = d0 + 4 * u < D ? *reinterpret_cast<const float4*>(kr + d0 + 4 * u)
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (d0 + 4 * u < D) {
+                            const float4 qv = *reinterpret_cast<const float4*>(s_q + d0 + 4 * u);
+                            acc[0] += qv.x * kv[u].x;
+                            acc[1] += qv.y * kv[u].y;
+                            acc[2] += qv.z * kv[u].z;
+                            acc[3] += qv.w * kv[u].w;
+                        }
+                    }
+                }
+            } else {
+                for (int d = 0; d < D; ++d) acc[d & 3] += s_q[d] * kr[d];
+            }
+            s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        }
+        const float bmax = wave_max_f32(s);
+        if (bmax == -INFINITY) continue;  // nothing visible in this block
+        const float m_new = fmaxf(m, bmax);
+        const float alpha = expf(m - m_new);  // 0 on the wave's first visible block (m = -inf)
+        const float p = vis ? expf(s - m_new) : 0.0f;
+        l = l * alpha + wave_sum_f32(p);
+        o0 *= alpha;
+        o1 *= alpha;
         m = m_new;
+        // P V: the V rows of 16 keys requested together; invisible keys have p = 0
+        const int nk = S - k0 < kWave ? S - k0 : kWave;
+        const float* vb = a.v + base + (int64_t)k0 * D;
+        for (int j0 = 0; j0 < nk; j0 += 16) {
+            float v0[16], v1[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const bool ok = j0 + u < nk;
+                v0[u] = ok && lane < D ? vb[(int64_t)(j0 + u) * D + lane] : 0.0f;
+                v1[u] = ok && lane + kWave < D ? vb[(int64_t)(j0 + u) * D + lane + kWave] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j0 + u));
+                o0 += pj * v0[u];
+                o1 += pj * v1[u];
+            }
+        }
+    }
+    // combine the waves' partials: a wave that saw no visible key has (-inf, 0, 0)
+    if (lane == 0) {
+        s_ml[0][wid] = m;
+        s_ml[1][wid] = l;
+    }
+    if (lane < D) s_o[wid][lane] = o0;
+    if (lane + kWave < D) s_o[wid][lane + kWave] = o1;
+    __syncthreads();
+    if (wid != 0) return;
+    float M = s_ml[0][0];
+#pragma unroll
+    for (int w = 1; w < kF32Waves; ++w) M = fmaxf(M, s_ml[0][w]);
+    float L = 0.0f, r0 = 0.0f, r1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kF32Waves; ++w) {
+        const float sc = s_ml[1][w] > 0.0f ? expf(s_ml[0][w] - M) : 0.0f;
+        L += s_ml[1][w] * sc;
+        if (lane < D) r0 += s_o[w][lane] * sc;
+        if (lane + kWave < D) r1 += s_o[w][lane + kWave] * sc;
     }
     float* orow = a.o + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
-    if (lane < D) orow[lane] = o0 / l;
-    if (lane + kWave < D) orow[lane + kWave] = o1 / l;
-    if (lane == 0 && a.lse) a.lse[((int64_t)b * a.T + i) * a.Hq + hq] = m + logf(l);
+    if (lane < D) orow[lane] = r0 / L;
+    if (lane + kWave < D) orow[lane + kWave] = r1 / L;
+    if (lane == 0 && a.lse) a.lse[((int64_t)b * a.T + i) * a.Hq + hq] = M + logf(L);
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -956,7 +1028,7 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.mask = mask; a.o = (float*)o; a.lse = lse;
         a.ctx_len = d.ctx_len; a.kv_row_off = d.kv_row_off; a.kv_rows_total = d.kv_rows_total;
         a.T = d.T; a.Hq = d.n_q_heads; a.G = G; a.D = d.head_dim; a.scale = scale;
-        tree_attn_f32_kernel<<<dim3(d.T, (d.n_q_heads + 3) / 4, d.batch), 256, 0, stream>>>(a);
+        tree_attn_f32_kernel<<<dim3(d.T, d.n_q_heads, d.batch), kF32Waves * 64, 0, stream>>>(a);
         return hipGetLastError();
     }
     const WsLayout w = ws_layout(d);
