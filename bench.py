@@ -66,6 +66,29 @@ def attention_flops_per_launch(w, mask_words, ctx_lens) -> int:
     return total
 
 
+def _cpu_all_cores(w, mask, t_tree, t_verify):
+    """The same oracle on every host core: P threads, each computing one distinct
+    attention layer (the oracle is a C library; its calls run outside the GIL),
+    wall time of the P layers, scaled to a full step."""
+    import concurrent.futures as cf
+    import oracle
+    from draft_tree_verification_eagle_amd import workload as wl
+
+    P = max(1, min(os.cpu_count() or 1, 16, w.layers))
+    inputs = []
+    for layer in range(P):
+        q, k, v, off, total = wl.attention_inputs(w, layer, device="cpu")
+        inputs.append((q[0].float().numpy(), k.float().numpy(), v.float().numpy()))
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=P) as ex:
+        list(ex.map(lambda x: oracle.attention(x[0], x[1], x[2], mask, w.ctx), inputs))
+    t_par = time.perf_counter() - t0
+    t_step = t_tree + w.layers * t_par / P + t_verify
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": P,
+            "sample": f"{P} attention layers on {P} threads in {t_par:.2f}s wall, scaled to {w.layers} layers "
+                      f"(tree and verification as in the one-thread figure)"}
+
+
 def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 8):
     """Oracle timing on a bounded sample: full tree + `layers` distinct attention
     layers + one verification, single-threaded, scaled to the full step
@@ -93,7 +116,9 @@ def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 
         oracle.verify_greedy(target[b], flat["flat_token"], flat["flat_parent"], w.depth)
     t_verify = time.perf_counter() - t0
     t_step = t_tree + w.layers * t_layer + t_verify
+    all_cores = _cpu_all_cores(w, flat["mask"], t_tree, t_verify)
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "all_cores": all_cores,
             "sample": f"tree build + {layers} of {w.layers} attention layers (fp64, {t_layers:.1f}s) + 1 verification, "
                       f"one thread; step time = tree {t_tree:.3f}s + {w.layers} x layer {t_layer:.2f}s + verify "
                       f"{t_verify:.4f}s (the oracle evaluates only the rows its walk visits)",
@@ -193,8 +218,8 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama2_13b")
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -237,7 +262,9 @@ def main():
             vs.run(temperature, seed, 0)
         torch.cuda.synchronize()
 
-    def one_step(i, ev=None):
+    def one_step(i, ev=None, ev_start=None):
+        if ev_start is not None:
+            ev_start.record(stream)
         if graph is not None:
             graph.replay()
             return
@@ -255,23 +282,29 @@ def main():
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    step_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        one_step(i, None if graph is not None else evs[i])
+        one_step(i, None if graph is not None else evs[i], step_evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.3f}s)", file=sys.stderr, flush=True)
 
+    # per-step times from the events at each step's start
+    bounds = step_evs + [t_end]
+    step_ms = np.array([bounds[j].elapsed_time(bounds[j + 1]) for j in range(args.steps)])
+    attn_us = None
     # attention launch time: events around the 40 launches of each timed step
     if graph is None:
         attn_ms = [a.elapsed_time(b) for a, b in evs]
         ms_per_launch = float(np.median(attn_ms)) / n_attn
+        attn_us = np.array(attn_ms) * 1e3 / n_attn
     else:
         # graph mode: time the attention launches alone on the same stream
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,6 +376,11 @@ def main():
                           "flop_per_byte": round(flops_launch / bytes_launch, 1)},
         },
     }
+    pct = lambda x: {"p10": round(float(np.percentile(x, 10)), 4), "median": round(float(np.median(x)), 4),
+                     "p90": round(float(np.percentile(x, 90)), 4)}
+    out["distribution"] = {"step_ms": pct(step_ms)}
+    if attn_us is not None:
+        out["distribution"]["attention_us_per_launch"] = pct(attn_us)
     if extras is not None:
         out["around_step"] = extras
     if not args.no_cpu_baseline:
