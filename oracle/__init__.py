@@ -53,9 +53,10 @@ def lib():
         L.orc_flatten_static.argtypes = [i32, P, i32, P, P, P]
         L.orc_rope.argtypes = [i32, i32, i32, P, f64, P, P]
         L.orc_kv_commit.argtypes = [i32, i32, i32, P, i32, i64, i64, i64, P, P]
+        L.orc_draft_subtree.argtypes = [i32, P, P, i32, P, i32, i32, P, P, P, P, P]
         for f in ("orc_tree_shape", "orc_expand", "orc_rerank", "orc_flatten", "orc_attention",
                   "orc_verify_greedy", "orc_verify_sampled", "orc_flatten_static", "orc_rope",
-                  "orc_kv_commit"):
+                  "orc_kv_commit", "orc_draft_subtree"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -216,6 +217,22 @@ def kv_commit(cache, ctx_len: int, T: int, accept_len: int, path, row0: int = 0)
                            cache.ctypes.data_as(C.c_void_p), _p(nc)):
         raise ValueError("accepted path is not a strictly increasing run of tree rows")
     return int(nc[0])
+
+
+def draft_subtree(tree: dict, frontier, ctx_len: int, T_sub: int):
+    """Rows of the draft-side attention for one sequence's frontier: dict(sub_node,
+    sub_parent, position [T_sub], mask [T_sub][T_sub] uint8, query_row [len(frontier)])."""
+    par = _c(tree["parent"], np.int32); dep = _c(tree["depth"], np.int32)
+    fr = _c(frontier, np.int32)
+    out = {k: np.zeros(T_sub, np.int32) for k in ("sub_node", "sub_parent", "position")}
+    mask = np.zeros((T_sub, T_sub), np.uint8)
+    qr = np.zeros(max(len(fr), 1), np.int32)
+    if lib().orc_draft_subtree(len(par), _p(par), _p(dep), len(fr), _p(fr), int(ctx_len), int(T_sub),
+                               _p(out["sub_node"]), _p(out["sub_parent"]), _p(out["position"]), _p(mask), _p(qr)):
+        raise ValueError("the frontier's root paths do not fit T_sub rows, or a frontier id is not a node")
+    out["mask"] = mask
+    out["query_row"] = qr[:len(fr)]
+    return out
 
 
 # ---------------------------------------------------------------------------

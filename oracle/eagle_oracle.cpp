@@ -552,4 +552,52 @@ int orc_kv_commit(int T, int ctx_len, int accept_len, const int* path, int n_hea
     return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Draft-side attention rows (EAGLE-2 page, two-stage passage: the m frontier
+// nodes are fed to the draft model; EAGLE page: that model is one decoder layer
+// which, like the target, must see each token's own history only).  The query
+// of frontier node f attends to the context and to f's root path.  The rows
+// used: U = the union of the frontier nodes' root paths, flattened in ascending
+// node id (a topological order), padded to T_sub rows.  For row r < |U|:
+// sub_node = its node id, sub_parent = its parent's row (-1 for the root),
+// position = ctx_len + depth.  Padding rows: node -1, parent -1, position
+// ctx_len, and they see only themselves.  mask[r][c] = 1 iff row c lies on the
+// root-to-r path (r included).  query_row[j] = the row of frontier[j].
+// Returns 0, or -1 if |U| > T_sub or a frontier id is not a node.
+// ---------------------------------------------------------------------------
+int orc_draft_subtree(int n_nodes, const int* parent, const int* depth, int n_frontier, const int* frontier,
+                      int ctx_len, int T_sub, int* sub_node, int* sub_parent, int* position,
+                      unsigned char* mask, int* query_row) {
+    std::vector<char> in(n_nodes, 0);
+    for (int j = 0; j < n_frontier; ++j) {
+        if (frontier[j] < 0 || frontier[j] >= n_nodes) return -1;
+        for (int x = frontier[j]; x >= 0; x = parent[x]) in[x] = 1;
+    }
+    std::vector<int> row_of(n_nodes, -1);
+    int U = 0;
+    for (int x = 0; x < n_nodes; ++x) {
+        if (!in[x]) continue;
+        if (U >= T_sub) return -1;
+        row_of[x] = U;
+        sub_node[U] = x;
+        ++U;
+    }
+    std::memset(mask, 0, (size_t)T_sub * T_sub);
+    for (int r = 0; r < T_sub; ++r) {
+        if (r >= U) {
+            sub_node[r] = -1;
+            sub_parent[r] = -1;
+            position[r] = ctx_len;
+            mask[(size_t)r * T_sub + r] = 1;
+            continue;
+        }
+        const int x = sub_node[r];
+        sub_parent[r] = parent[x] >= 0 ? row_of[parent[x]] : -1;
+        position[r] = ctx_len + depth[x];
+        for (int y = x; y >= 0; y = parent[y]) mask[(size_t)r * T_sub + row_of[y]] = 1;
+    }
+    for (int j = 0; j < n_frontier; ++j) query_row[j] = row_of[frontier[j]];
+    return 0;
+}
+
 }  // extern "C"

@@ -1,6 +1,6 @@
-"""Pins for the oracle's static-tree flattening, rotary at tree positions and KV
-commit of the accepted path: each check ties them to something other than
-themselves.
+"""Pins for the oracle's static-tree flattening, rotary at tree positions, KV
+commit of the accepted path and draft-side attention rows: each check ties them
+to something other than themselves.
 
 Sources of truth used here:
   * the dynamic-tree flattening (pinned on its own by ancestor closure, the
@@ -14,7 +14,11 @@ Sources of truth used here:
   * consistency with plain autoregressive decoding (EAGLE-2 page, passage after
     the two stages): a committed cache must equal the cache that decoding the
     accepted tokens one by one would have produced, for a model whose K/V rows
-    depend only on the token prefix.
+    depend only on the token prefix;
+  * for the draft side: the union of the frontier's root paths by parent walks,
+    the frontier recomputed from its definition (the m best nodes of the last
+    layer by value, then id), and softmax attention over exactly the context and
+    a frontier node's root path.
 """
 import json
 import os
@@ -250,3 +254,89 @@ def test_kv_commit_rejects_non_paths(orc, al, path):
     cache = np.zeros((1, 20, 4), np.float32)
     with pytest.raises(ValueError):
         orc.kv_commit(cache, 4, 6, al, path)
+
+
+# ---------------------------------------------------------------------------
+# Draft-side attention rows: the frontier's root paths as a small flattened tree
+# ---------------------------------------------------------------------------
+def _frontier_of_layer(tree, layer, m):
+    """Frontier consumed by draft layer `layer` (>= 2): the min(m, |layer - 1|) nodes
+    of depth layer - 1 with the largest value, ties to the lower id."""
+    ids = np.nonzero(tree["depth"] == layer - 1)[0]
+    order = np.lexsort((ids, -tree["value"][ids].astype(np.float64)))
+    return ids[order][:min(m, len(ids))]
+
+
+def _root_path(tree, x):
+    path = []
+    while x >= 0:
+        path.append(int(x)); x = int(tree["parent"][x])
+    return path
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_draft_subtree_is_union_of_root_paths(orc, seed):
+    rng = np.random.default_rng(1100 + seed)
+    V = 16; depth = int(rng.integers(2, 6)); k = int(rng.integers(1, 5)); m = int(rng.integers(1, 5))
+    fs, cap = orc.tree_shape(depth, k, m)
+    z = rng.normal(0, 2, (int(fs.sum()), V)).astype(np.float32)
+    tree = orc.expand(z, 2, depth, k, m)
+    ctx = int(rng.integers(0, 30))
+    for layer in range(2, depth + 1):
+        fr = _frontier_of_layer(tree, layer, m)
+        T_sub = 1 + len(fr) * (layer - 1) + int(rng.integers(0, 3))
+        st = orc.draft_subtree(tree, fr, ctx, T_sub)
+        U = sorted(set(x for f in fr for x in _root_path(tree, f)))
+        nU = len(U)
+        assert list(st["sub_node"][:nU]) == U and all(x == -1 for x in st["sub_node"][nU:])
+        row = {x: r for r, x in enumerate(U)}
+        for r, x in enumerate(U):
+            assert st["position"][r] == ctx + tree["depth"][x]
+            seen = {int(c) for c in np.nonzero(st["mask"][r])[0]}
+            assert seen == {row[y] for y in _root_path(tree, x)}
+            p = tree["parent"][x]
+            assert st["sub_parent"][r] == (row[p] if p >= 0 else -1)
+        for r in range(nU, T_sub):
+            assert set(np.nonzero(st["mask"][r])[0]) == {r} and st["position"][r] == ctx
+        assert [U[q] for q in st["query_row"]] == [int(f) for f in fr]
+
+
+def test_draft_subtree_attention_is_context_plus_root_path(orc):
+    """Attention of a frontier node's row over the flattened rows equals softmax
+    attention over exactly the context and that node's root path."""
+    rng = np.random.default_rng(77)
+    V, depth, k, m = 20, 4, 3, 3
+    fs, cap = orc.tree_shape(depth, k, m)
+    z = rng.normal(0, 2, (int(fs.sum()), V)).astype(np.float32)
+    tree = orc.expand(z, 0, depth, k, m)
+    layer, ctx, H, D = 4, 23, 2, 16
+    fr = _frontier_of_layer(tree, layer, m)
+    T_sub = 1 + len(fr) * (layer - 1)
+    st = orc.draft_subtree(tree, fr, ctx, T_sub)
+    n_nodes = len(tree["parent"])
+    # node-indexed draft K/V and per-node queries
+    kc = rng.normal(0, 1, (H, ctx, D)).astype(np.float32); vc = rng.normal(0, 1, (H, ctx, D)).astype(np.float32)
+    kn = rng.normal(0, 1, (H, n_nodes, D)).astype(np.float32); vn = rng.normal(0, 1, (H, n_nodes, D)).astype(np.float32)
+    qn = rng.normal(0, 1, (n_nodes, H, D)).astype(np.float32)
+    nodes = np.where(st["sub_node"] >= 0, st["sub_node"], 0)
+    k = np.concatenate([kc, kn[:, nodes]], axis=1); v = np.concatenate([vc, vn[:, nodes]], axis=1)
+    q = qn[nodes]
+    o, lse = orc.attention(q, k, v, st["mask"], ctx)
+    for j, f in enumerate(fr):
+        path = _root_path(tree, f)
+        keys = np.concatenate([kc, kn[:, path]], axis=1).astype(np.float64)
+        vals = np.concatenate([vc, vn[:, path]], axis=1).astype(np.float64)
+        for h in range(H):
+            sc = keys[h] @ qn[f, h].astype(np.float64) / np.sqrt(D)
+            w = np.exp(sc - sc.max()); w /= w.sum()
+            np.testing.assert_allclose(o[st["query_row"][j], h], w @ vals[h], rtol=1e-12, atol=1e-12)
+
+
+def test_draft_subtree_rejects_overflow(orc):
+    tree = dict(parent=np.array([-1, 0, 0, 1, 2]), depth=np.array([0, 1, 1, 2, 2]))
+    with pytest.raises(ValueError):
+        orc.draft_subtree(tree, [3, 4], 0, 4)  # needs 5 rows
+    with pytest.raises(ValueError):
+        orc.draft_subtree(tree, [9], 0, 8)
+    st = orc.draft_subtree(tree, [3, 4], 0, 5)
+    assert list(st["sub_node"]) == [0, 1, 2, 3, 4]
