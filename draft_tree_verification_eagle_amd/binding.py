@@ -67,6 +67,9 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
     L.eagle_tree_mask_static.argtypes = [i32, i32, P, P, P, P, P, P]; L.eagle_tree_mask_static.restype = C.c_int
     L.eagle_tree_rope.argtypes = [P, P, C.c_double, P, P, P]; L.eagle_tree_rope.restype = C.c_int
     L.eagle_kv_commit.argtypes = [P, P, P, P, P, P, P]; L.eagle_kv_commit.restype = C.c_int
+    L.eagle_draft_subtree_rows.argtypes = [P, i32]; L.eagle_draft_subtree_rows.restype = i32
+    L.eagle_draft_subtree.argtypes = [P, i32, P, P, P, P, P, P, P, P]; L.eagle_draft_subtree.restype = C.c_int
+    L.eagle_kv_gather.argtypes = [P, P, C.c_int64, C.c_int64, P, P, P, P, P]; L.eagle_kv_gather.restype = C.c_int
     L.eagle_status_string.argtypes = [C.c_int]; L.eagle_status_string.restype = C.c_char_p
     return L
 
@@ -236,3 +239,25 @@ def eagle_kv_commit(desc: CommitDesc, accept_len, accept_path, k_layers, v_layer
     VA = (C.c_void_p * max(n, 1))(*[_ptr(t) for t in v_layers])
     _check("eagle_kv_commit", _lib.eagle_kv_commit(C.byref(desc), _ptr(accept_len), _ptr(accept_path), KA, VA,
                                                    _ptr(new_ctx_len), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Draft-side attention rows and the row gather into the KV cache.
+# ---------------------------------------------------------------------------
+def eagle_draft_subtree_rows(cfg: TreeCfg, layer: int) -> int:
+    return _lib.eagle_draft_subtree_rows(C.byref(cfg), layer)
+
+
+def eagle_draft_subtree(cfg: TreeCfg, layer: int, state: TreeState, ctx_len, sub_node, sub_parent, position, mask,
+                        query_row, stream=None):
+    st = state.c_struct()
+    _check("eagle_draft_subtree", _lib.eagle_draft_subtree(
+        C.byref(cfg), int(layer), C.byref(st), _ptr(ctx_len), _ptr(sub_node), _ptr(sub_parent), _ptr(position),
+        _ptr(mask), _ptr(query_row), _stream(stream)))
+
+
+def eagle_kv_gather(desc: AttnDesc, rows, src_rows_per_seq: int, src_rows_total: int, src_k, src_v, k_cache,
+                    v_cache, stream=None):
+    _check("eagle_kv_gather", _lib.eagle_kv_gather(
+        C.byref(desc), _ptr(rows), int(src_rows_per_seq), int(src_rows_total), _ptr(src_k), _ptr(src_v),
+        _ptr(k_cache), _ptr(v_cache), _stream(stream)))

@@ -1,6 +1,7 @@
 // C ABI of the tree-verification library: host-side validation, then launches on
 // the caller's stream.  See include/eagle_tree.h for the contract of each call.
 #include <math.h>
+#include <stdint.h>
 
 #include "launchers.hpp"
 
@@ -210,6 +211,51 @@ int eagle_kv_commit(const eagle_commit_desc* desc, const int32_t* accept_len, co
     }
     return from_hip(eagle::launch_kv_commit(*d, accept_len, accept_path, k_layers, v_layers, new_ctx_len,
                                             stream));
+}
+
+int32_t eagle_draft_subtree_rows(const eagle_tree_cfg* cfg, int32_t layer) {
+    const int32_t F = eagle_tree_frontier_rows(cfg, layer);
+    if (F < 0) return -1;
+    const int64_t t = 1 + (int64_t)F * (layer - 1);
+    return t > INT32_MAX ? -1 : (int32_t)t;
+}
+
+int eagle_draft_subtree(const eagle_tree_cfg* cfg, int32_t layer, const eagle_tree_state* state,
+                        const int32_t* ctx_len, int32_t* sub_node, int32_t* sub_parent, int32_t* position,
+                        uint64_t* mask, int32_t* query_row, hipStream_t stream) {
+    int32_t cap = 0;
+    const int st = tree_limits(cfg, &cap);
+    if (st != EAGLE_OK) return st;
+    if (layer < 1 || layer > cfg->depth || !state_ok(state)) return EAGLE_ERR_INVALID_ARG;
+    const int32_t T_sub = eagle_draft_subtree_rows(cfg, layer);
+    if (T_sub < 1) return EAGLE_ERR_INVALID_ARG;
+    if (T_sub > EAGLE_MAX_TREE_ROWS) return EAGLE_ERR_UNSUPPORTED;
+    if (cfg->batch == 0) return EAGLE_OK;
+    if (!ctx_len || !sub_node || !sub_parent || !position || !mask || !query_row) return EAGLE_ERR_INVALID_ARG;
+    const int F = eagle_tree_frontier_rows(cfg, layer);
+    return from_hip(eagle::launch_draft_subtree(*cfg, layer, cap, F, T_sub, *state, ctx_len, sub_node, sub_parent,
+                                                position, mask, query_row, stream));
+}
+
+int eagle_kv_gather(const eagle_attn_desc* desc, const int32_t* rows, int64_t src_rows_per_seq,
+                    int64_t src_rows_total, const void* src_k, const void* src_v, void* k_cache, void* v_cache,
+                    hipStream_t stream) {
+    const eagle_attn_desc* d = desc;
+    if (!d || d->batch < 0 || d->T < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->kv_rows_total < 0 ||
+        src_rows_per_seq < 1 || src_rows_total < 0)
+        return EAGLE_ERR_INVALID_ARG;
+    if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
+    const int align = d->dtype == EAGLE_BF16 ? 8 : 4;
+    if (d->T > EAGLE_MAX_TREE_ROWS || d->head_dim > 256 || d->head_dim % align != 0 || d->batch > EAGLE_MAX_BATCH ||
+        d->n_kv_heads > 65535)
+        return EAGLE_ERR_UNSUPPORTED;
+    if (src_rows_total < (int64_t)d->batch * src_rows_per_seq) return EAGLE_ERR_INVALID_ARG;
+    if (d->batch == 0) return EAGLE_OK;
+    if (!rows || !src_k || !src_v || !k_cache || !v_cache || !d->ctx_len || !d->kv_row_off) return EAGLE_ERR_INVALID_ARG;
+    if (((uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+        return EAGLE_ERR_INVALID_ARG;
+    return from_hip(eagle::launch_kv_gather(*d, rows, src_rows_per_seq, src_rows_total, src_k, src_v, k_cache,
+                                            v_cache, stream));
 }
 
 const char* eagle_status_string(int status) {

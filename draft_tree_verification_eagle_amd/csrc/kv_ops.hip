@@ -1,7 +1,8 @@
 // Kernels around the verification step: the mask of a caller-given static tree,
-// rotary position encoding of the tree rows at their positions, and the KV
-// commit of the accepted path.  All three are small (tens of KB to a few MB per
-// step) and latency-bound; each is one launch.
+// rotary position encoding of the tree rows at their positions, the KV commit of
+// the accepted path, the rows of the draft-side attention and a row gather into
+// the KV cache.  All are small (tens of KB to a few MB per call) and
+// latency-bound; each is one launch.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -10,6 +11,8 @@
 
 namespace eagle {
 namespace {
+
+constexpr int kWave = 64;  // lanes per wavefront
 
 // ---------------------------------------------------------------------------
 // Static tree: one wave per sequence, lane i = row i.  Row i's ancestors are
@@ -212,7 +215,168 @@ __global__ __launch_bounds__(64) void kv_commit_kernel(int T, int depth, int row
     }
 }
 
+// ---------------------------------------------------------------------------
+// Draft-side attention rows.  One workgroup per sequence.  Each frontier node
+// marks its root path in an LDS bitmap over the nodes created so far; a node's
+// row is the number of marked nodes below it (per-word prefix of popcounts plus
+// the bits below it in its word), so rows follow ascending node id.  Rows whose
+// ids rank past T_sub are dropped (never the case for a consistent tree: the
+// frontier's root paths hold at most 1 + F (layer - 1) nodes), and since
+// ancestors have smaller ids the kept rows stay ancestor-closed.
+// ---------------------------------------------------------------------------
+constexpr int kSubThreads = 256;
+constexpr int kFlagWords = EAGLE_MAX_CAPACITY / 32;
+
+__global__ __launch_bounds__(kSubThreads) void draft_subtree_kernel(
+    int cap, int m, int F, int T_sub, int root_only, const int32_t* __restrict__ parent, const int32_t* __restrict__ depth,
+    const int32_t* __restrict__ frontier, const int32_t* __restrict__ n_nodes, const int32_t* __restrict__ ctx_len,
+    int32_t* __restrict__ sub_node, int32_t* __restrict__ sub_parent, int32_t* __restrict__ position,
+    uint64_t* __restrict__ mask, int32_t* __restrict__ query_row) {
+    __shared__ uint32_t flags[kFlagWords];
+    __shared__ int base[kFlagWords + 1];
+    __shared__ int32_t s_par[EAGLE_MAX_TREE_ROWS];
+    __shared__ int32_t s_node[EAGLE_MAX_TREE_ROWS];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (root_only) {
+        // draft layer 1: the root is the only query and the only row; the tree state
+        // is not read (the first expand has not run yet)
+        if (tid == 0) {
+            sub_node[b] = 0;
+            sub_parent[b] = -1;
+            position[b] = ctx_len[b];
+            mask[b] = 1ull;
+        }
+        for (int j = tid; j < m; j += kSubThreads) query_row[(size_t)b * m + j] = j == 0 ? 0 : -1;
+        return;
+    }
+    int n = n_nodes[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const int nw = (n + 31) >> 5;
+    for (int w = tid; w < kFlagWords; w += kSubThreads) flags[w] = 0;
+    if (tid < T_sub) s_node[tid] = -1;
+    __syncthreads();
+    if (tid < F) {  // F <= T_sub <= 64 past layer 1
+        int x = frontier[(size_t)b * m + tid];
+        for (int steps = 0; x >= 0 && x < n && steps <= 255; ++steps) {
+            atomicOr(&flags[x >> 5], 1u << (x & 31));
+            x = parent[(size_t)b * cap + x];
+        }
+    }
+    __syncthreads();
+    // exclusive prefix of the words' popcounts (kFlagWords = 128: two words per lane of wave 0)
+    if (tid < kWave) {
+        const int c0 = __popc(flags[2 * lane]), c1 = __popc(flags[2 * lane + 1]);
+        int incl = c0 + c1;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += o;
+        }
+        base[2 * lane] = incl - c0 - c1;
+        base[2 * lane + 1] = incl - c1;
+        if (lane == kWave - 1) base[kFlagWords] = incl;
+    }
+    __syncthreads();
+    auto row_of = [&](int x) {
+        return base[x >> 5] + __popc(flags[x >> 5] & ((1u << (x & 31)) - 1u));
+    };
+    auto marked = [&](int x) { return x >= 0 && x < n && ((flags[x >> 5] >> (x & 31)) & 1u); };
+    for (int x = tid; x < nw * 32; x += kSubThreads) {
+        if (marked(x)) {
+            const int r = row_of(x);
+            if (r < T_sub) s_node[r] = x;
+        }
+    }
+    __syncthreads();
+    if (tid < T_sub) {
+        const int x = s_node[tid];
+        int pr = -1;
+        if (x >= 0) {
+            const int p = parent[(size_t)b * cap + x];
+            if (marked(p)) pr = row_of(p);
+            if (pr >= T_sub) pr = -1;
+        }
+        s_par[tid] = pr;
+    }
+    __syncthreads();
+    if (tid < T_sub) {
+        const int x = s_node[tid];
+        uint64_t bits = 1ull << tid;
+        if (x >= 0) {
+            // each step moves to an earlier row, so the walk ends within T_sub steps
+            for (int r = s_par[tid]; r >= 0; r = s_par[r]) bits |= 1ull << r;
+        }
+        const size_t o = (size_t)b * T_sub + tid;
+        sub_node[o] = x;
+        sub_parent[o] = s_par[tid];
+        position[o] = ctx_len[b] + (x >= 0 ? depth[(size_t)b * cap + x] : 0);
+        mask[o] = bits;
+    }
+    for (int j = tid; j < m; j += kSubThreads) {
+        int qr = -1;
+        if (j < F) {
+            const int f = frontier[(size_t)b * m + j];
+            if (marked(f)) {
+                const int r = row_of(f);
+                qr = r < T_sub ? r : -1;
+            }
+        }
+        query_row[(size_t)b * m + j] = qr;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row gather: one wave per (row, KV head, sequence); lane = 16-byte chunk of the
+// row, K and V.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void kv_gather_kernel(int T, int row_chunks, int64_t kv_rows_total,
+                                                       const int32_t* __restrict__ ctx_len,
+                                                       const int64_t* __restrict__ kv_row_off,
+                                                       int64_t src_rows_per_seq, int64_t src_rows_total,
+                                                       const int32_t* __restrict__ rows,
+                                                       const char* __restrict__ src_k,
+                                                       const char* __restrict__ src_v, char* k, char* v) {
+    const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int64_t dst = kv_row_off[b] + (int64_t)ctx_len[b] + r;
+    if (dst < 0 || dst >= kv_rows_total) return;
+    int64_t x = rows[(size_t)b * T + r];
+    if (x < 0 || x >= src_rows_per_seq) x = 0;
+    const int64_t src = (int64_t)b * src_rows_per_seq + x;
+    if (src >= src_rows_total) return;
+    const size_t row_bytes = (size_t)row_chunks * 16;
+    const size_t so = ((size_t)g * src_rows_total + src) * row_bytes, dofs = ((size_t)g * kv_rows_total + dst) * row_bytes;
+    for (int c = lane; c < row_chunks; c += 64) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(src_k + so + (size_t)c * 16);
+        const uint4 vv = *reinterpret_cast<const uint4*>(src_v + so + (size_t)c * 16);
+        *reinterpret_cast<uint4*>(k + dofs + (size_t)c * 16) = kk;
+        *reinterpret_cast<uint4*>(v + dofs + (size_t)c * 16) = vv;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_draft_subtree(const eagle_tree_cfg& cfg, int layer, int cap, int F, int T_sub,
+                                const eagle_tree_state& st, const int32_t* ctx_len, int32_t* sub_node,
+                                int32_t* sub_parent, int32_t* position, uint64_t* mask, int32_t* query_row,
+                                hipStream_t stream) {
+    draft_subtree_kernel<<<cfg.batch, kSubThreads, 0, stream>>>(cap, cfg.m, F, T_sub, layer == 1 ? 1 : 0,
+                                                                 st.parent, st.depth,
+                                                                 st.frontier, st.n_nodes, ctx_len, sub_node,
+                                                                 sub_parent, position, mask, query_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_gather(const eagle_attn_desc& d, const int32_t* rows, int64_t src_rows_per_seq,
+                            int64_t src_rows_total, const void* src_k, const void* src_v, void* k, void* v,
+                            hipStream_t stream) {
+    const int elt = d.dtype == EAGLE_BF16 ? 2 : 4;
+    const int row_chunks = d.head_dim * elt / 16;
+    kv_gather_kernel<<<dim3(d.T, d.n_kv_heads, d.batch), 64, 0, stream>>>(
+        d.T, row_chunks, d.kv_rows_total, d.ctx_len, d.kv_row_off, src_rows_per_seq, src_rows_total, rows,
+        (const char*)src_k, (const char*)src_v, (char*)k, (char*)v);
+    return hipGetLastError();
+}
+
 
 hipError_t launch_mask_static(int batch, int T, const int32_t* flat_parent, const int32_t* ctx_len,
                               int32_t* flat_depth, int32_t* position, uint64_t* mask, hipStream_t stream) {

@@ -51,4 +51,13 @@ hipError_t launch_kv_commit(const eagle_commit_desc& d, const int32_t* accept_le
                             void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len,
                             hipStream_t stream);
 
+// Draft-side attention rows and the row gather into the KV cache.
+hipError_t launch_draft_subtree(const eagle_tree_cfg& cfg, int layer, int cap, int F, int T_sub,
+                                const eagle_tree_state& st, const int32_t* ctx_len, int32_t* sub_node,
+                                int32_t* sub_parent, int32_t* position, uint64_t* mask, int32_t* query_row,
+                                hipStream_t stream);
+hipError_t launch_kv_gather(const eagle_attn_desc& d, const int32_t* rows, int64_t src_rows_per_seq,
+                            int64_t src_rows_total, const void* src_k, const void* src_v, void* k, void* v,
+                            hipStream_t stream);
+
 }  // namespace eagle

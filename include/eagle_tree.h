@@ -13,6 +13,9 @@
  *   eagle_tree_rope         rotary position encoding of the tree rows at their positions
  *   eagle_kv_commit         move the accepted rows' K/V behind the context, as
  *                           autoregressive decoding would have left them
+ *   eagle_draft_subtree     rows, masks and positions of the draft model's attention
+ *                           at a draft layer (the frontier nodes' root paths)
+ *   eagle_kv_gather         copy rows (e.g. tree nodes' draft K/V) behind the context
  *
  * Pages defining the operations (cited by title and passage):
  *   EAGLE-2 page -- news write-up of "EAGLE-2: Faster Inference of Language Models
@@ -278,6 +281,47 @@ typedef struct {
 
 int eagle_kv_commit(const eagle_commit_desc* desc, const int32_t* accept_len, const int32_t* accept_path,
                     void* const* k_layers, void* const* v_layers, int32_t* new_ctx_len, hipStream_t stream);
+
+/* Draft-side attention rows (EAGLE-2 page, two-stage passage: the m best nodes of
+ * the last layer are fed to the draft model; EAGLE page: the draft model is one
+ * decoder layer whose tokens, like the target's, see the context and their own
+ * history only).  At draft layer `layer` (2..depth) the queries are the frontier
+ * nodes -- eagle_tree_frontier_rows(cfg, layer) of them, in state->frontier after
+ * eagle_tree_expand of layer - 1 -- and each attends to the context and to its own
+ * root path.  Per sequence, the union of those root paths is flattened in
+ * ascending node id (a topological order) into T_sub = eagle_draft_subtree_rows
+ * (cfg, layer) = 1 + F_layer * (layer - 1) rows:
+ *     sub_node   [batch][T_sub] node id, -1 for padding rows
+ *     sub_parent [batch][T_sub] parent's row, -1 for the root and padding
+ *     position   [batch][T_sub] ctx_len[b] + depth; padding: ctx_len[b]
+ *     mask       [batch][T_sub] uint64: bit c of row r iff row c is on the root-to-r
+ *                path (r included); a padding row sees only itself
+ *     query_row  [batch][m]     the row of frontier[j]; -1 for j >= F_layer
+ * The rows' draft K/V go behind the context with eagle_kv_gather (rows = sub_node),
+ * and eagle_tree_attention with T = T_sub then gives every row's draft attention;
+ * the frontier's are at query_row.  Layer 1's only query is the root (T_sub = 1).
+ * T_sub > EAGLE_MAX_TREE_ROWS is EAGLE_ERR_UNSUPPORTED; layer outside 1..depth is
+ * EAGLE_ERR_INVALID_ARG.  eagle_draft_subtree_rows returns -1 for an invalid cfg or
+ * layer. */
+int32_t eagle_draft_subtree_rows(const eagle_tree_cfg* cfg, int32_t layer);
+
+int eagle_draft_subtree(const eagle_tree_cfg* cfg, int32_t layer, const eagle_tree_state* state,
+                        const int32_t* ctx_len, int32_t* sub_node, int32_t* sub_parent, int32_t* position,
+                        uint64_t* mask, int32_t* query_row, hipStream_t stream);
+
+/* Row gather into the KV cache (the draft K/V of eagle_draft_subtree's rows, or of
+ * any per-sequence row list).  For sequence b and row r < desc->T, every KV head's
+ * row kv_row_off[b] + ctx_len[b] + r of k_cache / v_cache ([n_kv_heads]
+ * [kv_rows_total][head_dim]) receives row b * src_rows_per_seq + x of src_k / src_v
+ * ([n_kv_heads][src_rows_total][head_dim]), x = rows[b][r]; an x outside
+ * 0..src_rows_per_seq - 1 (padding, -1) reads row x = 0.  desc as for
+ * eagle_tree_attention (scale and host copies unused).  Destination rows outside
+ * the cache are skipped.  Supported: head_dim a multiple of 8 (BF16) or 4 (F32),
+ * <= 256; T <= 64; pointers 16-byte aligned; src_rows_total >= batch *
+ * src_rows_per_seq. */
+int eagle_kv_gather(const eagle_attn_desc* desc, const int32_t* rows, int64_t src_rows_per_seq,
+                    int64_t src_rows_total, const void* src_k, const void* src_v, void* k_cache, void* v_cache,
+                    hipStream_t stream);
 
 /* Human-readable name of a status code. */
 const char* eagle_status_string(int status);

@@ -289,3 +289,45 @@ def test_kv_commit_validation(eb):
     nul = (C.c_void_p * 2)(0x2000, 0)
     assert call(v=nul) == eb.EAGLE_ERR_INVALID_ARG
     assert L.eagle_kv_commit(None, f, f, ks, vs, f, None) == eb.EAGLE_ERR_INVALID_ARG
+
+
+def test_draft_subtree_rows_and_validation(eb):
+    L = eb.lib()
+    f = FAKE
+    cfg = eb.make_cfg(1, 32000, 6, 10, 10, 60)
+    assert [eb.eagle_draft_subtree_rows(cfg, l) for l in range(1, 7)] == [1, 11, 21, 31, 41, 51]
+    cfg5 = eb.make_cfg(16, 32000, 7, 8, 8, 60)
+    assert eb.eagle_draft_subtree_rows(cfg5, 7) == 49
+    assert eb.eagle_draft_subtree_rows(cfg, 0) == -1 and eb.eagle_draft_subtree_rows(cfg, 7) == -1
+    st = _state(eb)
+    args = [f] * 6
+    assert L.eagle_draft_subtree(C.byref(cfg), 0, C.byref(st), *args, None) == eb.EAGLE_ERR_INVALID_ARG
+    assert L.eagle_draft_subtree(C.byref(cfg), 7, C.byref(st), *args, None) == eb.EAGLE_ERR_INVALID_ARG
+    wide = eb.make_cfg(1, 2000, 3, 32, 32, 60)  # F_3 = 32: 1 + 32 * 2 = 65 rows
+    assert eb.eagle_draft_subtree_rows(wide, 3) == 65
+    assert L.eagle_draft_subtree(C.byref(wide), 3, C.byref(st), *args, None) == eb.EAGLE_ERR_UNSUPPORTED
+    assert L.eagle_draft_subtree(C.byref(cfg), 2, C.byref(st), None, f, f, f, f, f, None) == eb.EAGLE_ERR_INVALID_ARG
+    empty = eb.make_cfg(0, 32000, 6, 10, 10, 60)
+    assert L.eagle_draft_subtree(C.byref(empty), 2, C.byref(st), *args, None) == eb.EAGLE_OK
+
+
+def test_kv_gather_validation(eb):
+    L = eb.lib()
+    f = FAKE
+
+    def call(dtype=eb.EAGLE_BF16, batch=1, T=51, D=128, per=511, total=511, rows=f, sk=0x2000, sv=0x3000,
+             k=0x4000, v=0x5000, ctx=f, off=f):
+        d = eb.make_attn_desc(dtype, batch, T, 40, 40, D, None, None, 5000)
+        d.ctx_len = ctx; d.kv_row_off = off
+        return L.eagle_kv_gather(C.byref(d), rows, per, total, sk, sv, k, v, None)
+
+    assert call(batch=0) == eb.EAGLE_OK
+    assert call(T=0) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(T=65) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(D=120 + 4) == eb.EAGLE_ERR_UNSUPPORTED
+    assert call(per=0) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(batch=2, total=600) == eb.EAGLE_ERR_INVALID_ARG  # fewer source rows than 2 x 511
+    assert call(rows=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(sv=None) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(k=0x4008) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(ctx=None) == eb.EAGLE_ERR_INVALID_ARG

@@ -389,3 +389,130 @@ def test_kv_commit_no_layers_reports_lengths(lib, orc):
     eb.eagle_kv_commit(d, al, ap, [], [], new_ctx)
     torch.cuda.synchronize()
     assert new_ctx.cpu().tolist() == [13, 21]
+
+
+# ---------------------------------------------------------------------------
+# draft-side attention: rows of the frontier's root paths, gather, attention
+# ---------------------------------------------------------------------------
+def _frontier_of_layer(tree, layer, m):
+    ids = np.nonzero(tree["depth"] == layer - 1)[0]
+    order = np.lexsort((ids, -tree["value"][ids].astype(np.float64)))
+    return ids[order][:min(m, len(ids))]
+
+
+def _root_path(tree, x):
+    path = []
+    while x >= 0:
+        path.append(int(x)); x = int(tree["parent"][x])
+    return path
+
+
+def _subtree_buffers(w, T_sub, device="cuda"):
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(node=torch.full((w.batch, T_sub), 7, **i32), parent=torch.full((w.batch, T_sub), 7, **i32),
+                position=torch.full((w.batch, T_sub), 7, **i32),
+                mask=torch.full((w.batch, T_sub), 7, dtype=torch.int64, device=device),
+                query_row=torch.full((w.batch, w.m), 7, **i32))
+
+
+@pytest.mark.parametrize("name", ["llama2_13b", "batched_13b"])
+def test_draft_subtree_every_layer(lib, orc, name):
+    """After each expand, the rows of the next draft layer's attention equal the
+    oracle's (bit-exact), layer 1 (before any expand) being the root alone."""
+    eb, stepm, wl = lib
+    w = wl.CONFIGS[name]
+    say(f"[draft subtree] {name}, layers 1..{w.depth}")
+    vs = stepm.VerifyStep(w, layers=0)
+    trees = [orc.expand(vs.draft_np[b], int(vs.root_np[b]), w.depth, w.topk, w.m) for b in range(w.batch)]
+    for layer in range(1, w.depth + 1):
+        if layer >= 2:
+            eb.eagle_tree_expand(vs.cfg, layer - 1, vs.draft_layers[layer - 2], vs.root, vs.state, vs.expand_ws)
+        T_sub = eb.eagle_draft_subtree_rows(vs.cfg, layer)
+        buf = _subtree_buffers(w, T_sub)
+        eb.eagle_draft_subtree(vs.cfg, layer, vs.state, vs.ctx_len, buf["node"], buf["parent"], buf["position"],
+                               buf["mask"], buf["query_row"])
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in buf.items()}
+        for b in range(w.batch):
+            ctx = int(vs.ctx_lens_np[b])
+            fr = [0] if layer == 1 else _frontier_of_layer(trees[b], layer, w.m)
+            ref = orc.draft_subtree(trees[b], fr, ctx, T_sub)
+            np.testing.assert_array_equal(got["node"][b], ref["sub_node"])
+            np.testing.assert_array_equal(got["parent"][b], ref["sub_parent"])
+            np.testing.assert_array_equal(got["position"][b], ref["position"])
+            np.testing.assert_array_equal(got["mask"][b].view(np.uint64), mask_words(ref["mask"]))
+            qr = np.full(w.m, -1, np.int32); qr[:len(fr)] = ref["query_row"]
+            np.testing.assert_array_equal(got["query_row"][b], qr)
+
+
+def test_draft_attention_gather_end_to_end(lib, orc):
+    """Draft layer 4 of the 13B-shaped tree, ragged batch of 3: the rows' draft K/V
+    gathered behind each context (bit-exact), then tree attention; each frontier
+    node's output equals softmax attention over exactly its context and root path."""
+    eb, stepm, wl = lib
+    w = small(wl, batch=3, ctx_range=(100, 3000), n_q_heads=8, n_kv_heads=4, depth=6, topk=10, m=10, n=60,
+              vocab=3000, seed=31)
+    layer = 4
+    say(f"[draft attention] layer {layer}, ragged batch of {w.batch}")
+    vs = stepm.VerifyStep(w, layers=0)
+    for l in range(1, layer):
+        eb.eagle_tree_expand(vs.cfg, l, vs.draft_layers[l - 1], vs.root, vs.state, vs.expand_ws)
+    T_sub = eb.eagle_draft_subtree_rows(vs.cfg, layer)
+    buf = _subtree_buffers(w, T_sub)
+    eb.eagle_draft_subtree(vs.cfg, layer, vs.state, vs.ctx_len, buf["node"], buf["parent"], buf["position"],
+                           buf["mask"], buf["query_row"])
+    cap = vs.cap
+    g = torch.Generator(device="cuda").manual_seed(99)
+    Hkv, Hq, D = w.n_kv_heads, w.n_q_heads, w.head_dim
+    node_k = torch.randn((Hkv, w.batch * cap, D), generator=g, device="cuda").to(torch.bfloat16)
+    node_v = torch.randn((Hkv, w.batch * cap, D), generator=g, device="cuda").to(torch.bfloat16)
+    node_q = torch.randn((w.batch, cap, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    lens = vs.ctx_lens_np.astype(np.int64)
+    off = np.zeros(w.batch, np.int64); off[1:] = np.cumsum(lens + T_sub)[:-1]
+    total = int((lens + T_sub).sum())
+    k = torch.randn((Hkv, total, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((Hkv, total, D), generator=g, device="cuda").to(torch.bfloat16)
+    off_t = torch.from_numpy(off).cuda()
+    desc = eb.make_attn_desc(eb.EAGLE_BF16, w.batch, T_sub, Hq, Hkv, D, vs.ctx_len, off_t, total,
+                             ctx_len_host=vs.ctx_lens_np, kv_row_off_host=off)
+    eb.eagle_kv_gather(desc, buf["node"], cap, w.batch * cap, node_k, node_v, k, v)
+    torch.cuda.synchronize()
+    nodes = buf["node"].cpu().numpy()
+    for b in range(w.batch):
+        src = torch.from_numpy((np.where(nodes[b] >= 0, nodes[b], 0) + b * cap).astype(np.int64)).cuda()
+        r0 = int(off[b] + lens[b])
+        assert torch.equal(k[:, r0:r0 + T_sub], node_k[:, src]) and torch.equal(v[:, r0:r0 + T_sub], node_v[:, src])
+    # the rows' queries: each row's node query
+    q = torch.stack([node_q[b][torch.from_numpy(np.where(nodes[b] >= 0, nodes[b], 0).astype(np.int64)).cuda()]
+                     for b in range(w.batch)]).contiguous()
+    o = torch.empty_like(q)
+    ws = torch.zeros(max(eb.eagle_tree_attention_workspace(desc), 1), dtype=torch.uint8, device="cuda")
+    eb.eagle_tree_attention(desc, q, k, v, buf["mask"], o, None, ws)
+    torch.cuda.synchronize()
+    tree_par = vs.state.parent.cpu().numpy()
+    qr = buf["query_row"].cpu().numpy()
+    worst = 0.0
+    for b in range(w.batch):
+        ctx = int(lens[b]); r0 = int(off[b])
+        kc = k[:, r0:r0 + ctx].float().cpu().numpy().astype(np.float64)
+        vc = v[:, r0:r0 + ctx].float().cpu().numpy().astype(np.float64)
+        F = eb.eagle_tree_frontier_rows(vs.cfg, layer)
+        for j in range(F):
+            row = int(qr[b, j]); f = int(nodes[b, row])
+            path = []
+            x = f
+            while x >= 0:
+                path.append(x); x = int(tree_par[b, x])
+            pidx = torch.from_numpy(b * cap + np.array(path, dtype=np.int64)).cuda()
+            kp = node_k[:, pidx].float().cpu().numpy().astype(np.float64)
+            vp = node_v[:, pidx].float().cpu().numpy().astype(np.float64)
+            for h in (0, Hq - 1):
+                gkv = h // (Hq // Hkv)
+                keys = np.concatenate([kc[gkv], kp[gkv]]); vals = np.concatenate([vc[gkv], vp[gkv]])
+                qv = node_q[b, f, h].float().cpu().numpy().astype(np.float64)
+                sc = keys @ qv / np.sqrt(D)
+                wgt = np.exp(sc - sc.max()); wgt /= wgt.sum()
+                err = float(np.abs(o[b, row, h].float().cpu().numpy() - wgt @ vals).max())
+                worst = max(worst, err)
+    assert worst <= ATOL_BF16, f"max |draft attention - definition| = {worst}"
+    say(f"  worst |o - definition| = {worst:.2e}")
