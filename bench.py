@@ -147,6 +147,47 @@ def _graph_us(fn, reps):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def _time_draft_side(vs, w, stream, reps: int = 20):
+    """Draft-side attention at the last draft layer: the rows of the frontier's root
+    paths, the gather of their draft K/V behind a draft context of the same length
+    and shape as the target's, and one tree-attention call over them (graph replays)."""
+    import torch
+    from draft_tree_verification_eagle_amd import binding as eb
+
+    layer = w.depth
+    T_sub = eb.eagle_draft_subtree_rows(vs.cfg, layer)
+    dev = vs.ctx_len.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    node = torch.empty((w.batch, T_sub), **i32); par = torch.empty((w.batch, T_sub), **i32)
+    pos = torch.empty((w.batch, T_sub), **i32); qrow = torch.empty((w.batch, w.m), **i32)
+    msk = torch.empty((w.batch, T_sub), dtype=torch.int64, device=dev)
+    sub = lambda: eb.eagle_draft_subtree(vs.cfg, layer, vs.state, vs.ctx_len, node, par, pos, msk, qrow)
+    subtree_us = _graph_us(sub, reps)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(7)
+    Hkv, D = w.n_kv_heads, w.head_dim
+    node_k = torch.randn((Hkv, w.batch * vs.cap, D), generator=g, device=dev).to(dt)
+    node_v = torch.randn((Hkv, w.batch * vs.cap, D), generator=g, device=dev).to(dt)
+    lens = vs.ctx_lens_np.astype(np.int64)
+    off = np.zeros(w.batch, np.int64); off[1:] = np.cumsum(lens + T_sub)[:-1]
+    total = int((lens + T_sub).sum())
+    k = torch.randn((Hkv, total, D), generator=g, device=dev).to(dt)
+    v = torch.randn((Hkv, total, D), generator=g, device=dev).to(dt)
+    q = torch.randn((w.batch, T_sub, w.n_q_heads, D), generator=g, device=dev).to(dt)
+    o = torch.empty_like(q)
+    off_t = torch.from_numpy(off).to(dev)
+    desc = eb.make_attn_desc(eb.EAGLE_BF16 if w.dtype == "bf16" else eb.EAGLE_F32, w.batch, T_sub, w.n_q_heads,
+                             Hkv, D, vs.ctx_len, off_t, total, ctx_len_host=vs.ctx_lens_np, kv_row_off_host=off)
+    ws = torch.zeros(max(eb.eagle_tree_attention_workspace(desc), 1), dtype=torch.uint8, device=dev)
+    gather_us = _graph_us(lambda: eb.eagle_kv_gather(desc, node, vs.cap, w.batch * vs.cap, node_k, node_v, k, v),
+                          reps)
+    attn_us = _graph_us(lambda: eb.eagle_tree_attention(desc, q, k, v, msk, o, None, ws), reps)
+    return {"layer": layer, "rows": T_sub, "subtree_us": round(subtree_us, 3), "gather_us": round(gather_us, 3),
+            "attention_us": round(attn_us, 3),
+            "what": "rows of the frontier's root paths, their draft K/V gathered behind a draft context of the "
+                    "target's shape, one draft attention call"}
+
+
 def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
     """Rotary at the tree positions (one call per layer), KV commit of an accepted
     path (one call for all layers), the static-tree mask (graph replays, HIP
@@ -182,6 +223,8 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
     dep = torch.empty_like(vs.flat_depth); pos = torch.empty_like(vs.position); msk = torch.empty_like(vs.mask)
     static_us = _graph_us(lambda: eb.eagle_tree_mask_static(w.batch, w.T, fpd, vs.ctx_len, dep, pos, msk), reps)
 
+    draft = _time_draft_side(vs, w, stream)
+
     def decode_step():
         vs.tree()
         vs.rope()
@@ -207,6 +250,7 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
                       "what": f"K and V of the accepted rows moved behind the context in all {vs.n_layers} "
                               f"layers (path: the deepest root path of the tree)"},
         "mask_static": {"us_per_call": round(static_us, 3)},
+        "draft_side": draft,
         "timing": "graph replays of the calls, HIP events",
         "decode_step_with_rope_and_commit": {
             "ms": round(full_us / 1e3, 4), "steps_per_s": round(1e6 / full_us, 2),
