@@ -51,21 +51,22 @@ struct RowStats {
 };
 
 // ---------------------------------------------------------------------------
-// K6: kRowSplit workgroups of 256 threads per (row, sequence), all four on one
+// K6: kRowSplit workgroups of 512 threads per (row, sequence), all four on one
 // XCD (blockIdx.x mod 8) so the row is fetched from HBM once and re-read from
 // that XCD's L2.  Every workgroup finds the row's maximum and argmax over the
 // whole row (float4 loads, all in flight together for vocabularies up to 32768);
 // then, for sampling, workgroup q takes chunks [256 q, 256 q + 256) of the row's
-// 1024 contiguous token chunks (ch = ceil(V / 1024) tokens each; thread = chunk,
-// re-read from L2), with a 256-bit mask of the row's children in the chunk: it
+// 1024 contiguous token chunks (ch = ceil(V / 1024) tokens each; two threads per
+// chunk, re-read from L2), with a 256-bit mask of the row's children in the chunk: it
 // stores each chunk's fixed-point mass (children included) for the bonus draw and
 // the fp64 mass of the non-child tokens of its quarter.  Workgroup 0 also writes
 // the children, their fp64 masses, the argmax and the maximum.  Wave 0 of each
 // workgroup finds the children with one ballot (flattened order = lane order).
 // ---------------------------------------------------------------------------
 constexpr int kRowSplit = 4;
-constexpr int kRowThreads = 256;
-constexpr int kRowChunks = kRowSplit * kRowThreads;  // 1024 chunks per row
+constexpr int kRowThreads = 512;
+constexpr int kWgChunks = kRowThreads / 2;           // two threads per chunk
+constexpr int kRowChunks = kRowSplit * kWgChunks;    // 1024 chunks per row
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kRowBatch = 32;       // loads per thread in flight together
 constexpr int kMaxChunkTokens = 256;  // ceil(EAGLE_MAX_VOCAB / 1024)
@@ -156,8 +157,12 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
         const double fscale = ldexp(1.0, fixed_shift(V));
         const int ch = (V + kRowChunks - 1) / kRowChunks;
-        const int chunk = q * kRowThreads + tid;
+        const int chunk = q * kWgChunks + (tid >> 1), half = tid & 1;
         const int c0 = min(V, chunk * ch), c1 = min(V, c0 + ch);
+        // the pair of threads splits the chunk: the first takes the first
+        // ceil(ch / 2) tokens rounded up to a multiple of 4, the second the rest
+        const int hc = (((ch + 1) >> 1) + 3) & ~3;
+        const int s0 = half == 0 ? c0 : min(c1, c0 + hc), s1 = half == 0 ? min(c1, c0 + hc) : c1;
         uint64_t km[4] = {0, 0, 0, 0};  // bit d: token c0 + d is a child of the row
         for (int c = 0; c < nk; ++c) {
             const int d = s_kid_tok[c] - c0;
@@ -171,28 +176,32 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         uint64_t fm = 0;
         // 16-byte aligned chunk starts: vector loads
         const bool cvec = vec && (ch & 3) == 0;
-        for (int a0 = c0; a0 < c1; a0 += kRowBatch) {
+        for (int a0 = s0; a0 < s1; a0 += kRowBatch) {
             float zz[kRowBatch];
             if (cvec) {
 #pragma unroll
                 for (int u = 0; u < kRowBatch; u += 4) {
                     float4 v4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (a0 + u < c1) v4 = *reinterpret_cast<const float4*>(z + a0 + u);
+                    if (a0 + u < s1) v4 = *reinterpret_cast<const float4*>(z + a0 + u);
                     zz[u] = v4.x; zz[u + 1] = v4.y; zz[u + 2] = v4.z; zz[u + 3] = v4.w;
                 }
             } else {
 #pragma unroll
-                for (int u = 0; u < kRowBatch; ++u) zz[u] = a0 + u < c1 ? z[a0 + u] : 0.0f;
+                for (int u = 0; u < kRowBatch; ++u) zz[u] = a0 + u < s1 ? z[a0 + u] : 0.0f;
             }
-            const int o = a0 - c0;  // a multiple of 32: bits o .. o + 31 of the mask
-            uint64_t kw = km[0];
+            // bits o .. o + 31 of the chunk's child mask, which may straddle two words
+            const int o = a0 - c0, wo = o >> 6, sh = o & 63;
+            uint64_t lo = km[0], hi = km[1];
 #pragma unroll
             for (int w = 1; w < 4; ++w)
-                if ((o >> 6) == w) kw = km[w];
-            const uint32_t kb = (uint32_t)(kw >> (o & 63));
+                if (wo == w) {
+                    lo = km[w];
+                    hi = w + 1 < 4 ? km[w + 1] : 0;
+                }
+            const uint32_t kb = (uint32_t)(sh == 0 ? lo : (lo >> sh) | (hi << (64 - sh)));
 #pragma unroll
             for (int u = 0; u < kRowBatch; ++u) {
-                if (a0 + u < c1) {
+                if (a0 + u < s1) {
                     const double x = (double)zz[u] - (double)zmax;
                     const double e = exp_nonpos_f64(unit_temp ? x : x / temp);
                     fm += fixed_mass(e, fscale);
@@ -200,7 +209,10 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
                 }
             }
         }
-        chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
+        // the pair's integer masses add exactly
+        const uint32_t flo = __shfl_xor((uint32_t)fm, 1, kWave), fhi = __shfl_xor((uint32_t)(fm >> 32), 1, kWave);
+        fm += ((uint64_t)fhi << 32) | flo;
+        if (half == 0) chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
         s = block_sum_f64(s, s_red);
         if (tid == 0) out->rest[q] = s;
         if (q == 0 && tid < nk)
