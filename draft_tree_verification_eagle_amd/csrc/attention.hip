@@ -225,7 +225,7 @@ struct Split {
     int nt;          // tiles per unit
     int nwg;         // workgroups that take part
 };
-__device__ __forceinline__ Split make_split(int S, int units, int grid) {
+__host__ __device__ inline Split make_split(int S, int units, int grid) {
     Split sp;
     sp.nt = (S + kTileKeys - 1) / kTileKeys;
     sp.W = 4u * (uint32_t)sp.nt + kSegCost4;
@@ -237,7 +237,7 @@ __device__ __forceinline__ Split make_split(int S, int units, int grid) {
     return sp;
 }
 // First cost step of stretch v: floor(Wt * v / nwg).
-__device__ __forceinline__ uint32_t stretch_start(const Split& sp, int v) {
+__host__ __device__ inline uint32_t stretch_start(const Split& sp, int v) {
     return sp.q * (uint32_t)v + (sp.r * (uint32_t)v) / (uint32_t)sp.nwg;
 }
 // First tile (unit, tile) starting at or after cost step p; (units, 0) past the last.
@@ -256,7 +256,7 @@ __device__ __forceinline__ TilePos split_tile(const Split& sp, uint32_t p) {
     return tp;
 }
 // Workgroup (in list order) whose stretch holds cost step p.
-__device__ __forceinline__ int stretch_of(const Split& sp, uint32_t p) {
+__host__ __device__ inline int stretch_of(const Split& sp, uint32_t p) {
     int v = (int)((double)p * (double)sp.nwg / (double)sp.Wt);
     if (v > sp.nwg - 1) v = sp.nwg - 1;
     while (v + 1 < sp.nwg && stretch_start(sp, v + 1) <= p) ++v;
@@ -796,19 +796,42 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 constexpr int kMergeBatch = 8;
 constexpr int kRowBlocks = kUnitRows / 16;
 
+// Per merge workgroup, its unit and that unit's first and last stretch (where its
+// partials are), computed on the host when the context length is known there: the
+// word is read by workgroup index alone, together with the other launch arguments,
+// so the kernel starts its loads without the split arithmetic (about 0.9 us at its
+// start).  Entry: bit 31 set = unit in use, bits 16..23 unit, 8..15 first stretch,
+// 0..7 last stretch.  Up to kPlanWgs merge workgroups (64 units).
+constexpr int kPlanWgs = 256;
+struct MergePlan {
+    int n_wg;                       // workgroups covered (0: computed in the kernel)
+    uint32_t e[kPlanWgs];
+};
+static_assert(kGridWG <= 256, "stretch indices fit 8 bits");
+
 template <bool kHostLen>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg) {
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg, MergePlan plan) {
     const int tid = threadIdx.x;
-    const int units = a.Hkv * a.RG;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int unit = merge_unit_first(xcd, units) + j / kRowBlocks;
-    if (unit >= merge_unit_first(xcd + 1, units)) return;
-    const int g = unit / a.RG, rg = unit - g * a.RG;
-    const int S = (kHostLen ? a.ctx_h : a.ctx_len[0]) + a.T;
-    const Split sp = make_split(S, units, grid_wg);
-    const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
-    const int vf = stretch_of(sp, p0), vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
+    int unit, vf, vl;
+    if (kHostLen && plan.n_wg > 0) {
+        const uint32_t e = plan.e[blockIdx.x];
+        if (!(e >> 31)) return;
+        unit = (int)((e >> 16) & 0xFFu);
+        vf = (int)((e >> 8) & 0xFFu);
+        vl = (int)(e & 0xFFu);
+    } else {
+        const int units = a.Hkv * a.RG;
+        unit = merge_unit_first(xcd, units) + j / kRowBlocks;
+        if (unit >= merge_unit_first(xcd + 1, units)) return;
+        const int S = (kHostLen ? a.ctx_h : a.ctx_len[0]) + a.T;
+        const Split sp = make_split(S, units, grid_wg);
+        const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
+        vf = stretch_of(sp, p0);
+        vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
+    }
     if (vf == vl) return;  // written directly by the main kernel
+    const int g = unit / a.RG, rg = unit - g * a.RG;
     const int row = (j % kRowBlocks) * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
     const int rp = rg * kUnitRows + row;
@@ -1059,11 +1082,32 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
             tree_attn_bf16_kernel<false><<<kGridWG, kThreads, 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int merge_wg = 8 * ((d.n_kv_heads * RG + 7) / 8) * kRowBlocks;
+        const int units = d.n_kv_heads * RG;
+        const int merge_wg = 8 * ((units + 7) / 8) * kRowBlocks;
+        MergePlan plan;
+        plan.n_wg = 0;
+        if (a.ctx_h >= 0 && merge_wg <= kPlanWgs) {
+            // the same split the main kernel makes, and the same workgroup -> unit map
+            // the merge kernel would compute, evaluated here once
+            const Split sp = make_split(a.ctx_h + d.T, units, kGridWG);
+            for (int wg = 0; wg < merge_wg; ++wg) {
+                const int xcd = wg & 7, j = wg >> 3;
+                const int u = merge_unit_first(xcd, units) + j / kRowBlocks;
+                uint32_t e = 0;
+                if (u < merge_unit_first(xcd + 1, units)) {
+                    const uint32_t p0 = (uint32_t)u * sp.W + kSegCost4;
+                    const uint32_t vf = (uint32_t)stretch_of(sp, p0);
+                    const uint32_t vl = (uint32_t)stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
+                    e = (1u << 31) | ((uint32_t)u << 16) | (vf << 8) | vl;
+                }
+                plan.e[wg] = e;
+            }
+            plan.n_wg = merge_wg;
+        }
         if (a.ctx_h >= 0)
-            tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(a, kGridWG);
+            tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(a, kGridWG, plan);
         else
-            tree_attn_merge_kernel<false><<<merge_wg, 256, 0, stream>>>(a, kGridWG);
+            tree_attn_merge_kernel<false><<<merge_wg, 256, 0, stream>>>(a, kGridWG, plan);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
