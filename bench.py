@@ -379,7 +379,8 @@ def main():
         try:
             rec = json.load(open(TRAFFIC_FILE))
             src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-            if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+            # the counters describe one workload and one kernel source
+            if hashlib.sha256(src).hexdigest() == rec["source_sha256"] and rec.get("workload") == w.name:
                 traffic = rec["bytes_per_launch"]
         except (OSError, KeyError, ValueError):
             traffic = None
