@@ -338,11 +338,11 @@ __global__ __launch_bounds__(kFinishThreads) void expand_finish_kernel(
 // ---------------------------------------------------------------------------
 // K3: per sequence, the n first non-root nodes in (value desc, depth asc, id asc),
 // written in ascending id.  Node keys pack the three into one unique 64-bit
-// value, larger = earlier.  Up to kRankMax candidates (one per thread): a node's
-// rank is the number of larger keys (threads sweep the keys' value words in LDS,
-// four per broadcast read, and the full keys only where value words tie), the
-// node is kept iff rank < n, and its output slot is the number of kept nodes with
-// a smaller id (a block prefix count of ballots).  Larger trees: one LDS bitonic sort, then the n first ids sorted
+// value, larger = earlier.  Up to kRankMax candidates (one per thread): the n-th
+// largest key is found by an 8-pass radix select (8-bit digits from the top, an
+// LDS histogram per pass), the n nodes whose keys are at least that are kept, and
+// a kept node's output slot is the number of kept nodes with a smaller id (a
+// block prefix count of ballots).  Larger trees: one LDS bitonic sort, then the n first ids sorted
 // again ascending.
 // ---------------------------------------------------------------------------
 constexpr int kRankMax = 1024;  // a multiple of 16, at most EAGLE_MAX_CAPACITY / 2
@@ -360,47 +360,58 @@ __global__ __launch_bounds__(1024) void rerank_kernel(int cap, int n, const floa
     __shared__ __attribute__((aligned(16))) uint64_t keys[EAGLE_MAX_CAPACITY];
     __shared__ uint64_t sel[EAGLE_MAX_TREE_ROWS];
     __shared__ int s_wave_kept[1024 / kWave];
+    __shared__ int s_pick[2];  // radix select: chosen digit, remaining rank
     const int b = blockIdx.x, tid = threadIdx.x;
     const int N = cap - 1;
     if (N <= kRankMax) {
-        // hi[j]: the value word of node j + 1's key (its top 32 bits).  A sweep reads
-        // four of them per broadcast read: rank = #(larger value words) + #(equal value
-        // words with a larger full key).  Only waves holding keys sweep, and the full
-        // keys are swept only by a wave in which some node's value word is not unique.
-        uint32_t* hi = reinterpret_cast<uint32_t*>(keys + kRankMax);  // past the keys: N16 <= kRankMax
         const int lane = tid & (kWave - 1), wid = tid / kWave;
-        const int N16 = (N + 15) & ~15;
-        const uint64_t mine = tid < N ? rerank_key(value, depth, b, cap, tid + 1) : 0;
-        for (int j = tid; j < N16; j += blockDim.x) {
-            const uint64_t kj = j == tid ? mine : 0;  // pads: key 0, value word 0
-            keys[j] = kj;
-            hi[j] = (uint32_t)(kj >> 32);
-        }
+        const uint64_t mine = tid < N ? rerank_key(value, depth, b, cap, tid + 1) : 0;  // real keys are > 0
+        // radix select of the n-th largest key, 8 bits a pass from the top: each pass
+        // counts the candidates (keys agreeing with the digits chosen so far) per next
+        // digit, and wave 0 picks the digit holding the remaining rank
+        uint32_t* hist = reinterpret_cast<uint32_t*>(keys);  // two 256-bin histograms
+        for (int i = tid; i < 512; i += blockDim.x) hist[i] = 0;
         __syncthreads();
-        int rank = 0;
-        if (wid * kWave < N) {
-            const uint32_t h = (uint32_t)(mine >> 32);
-            int eq = 0;  // nodes with the same value word, this one included
-            for (int j = 0; j < N16; j += 16) {
-                uint4 hh[4];
+        uint64_t prefix = 0;
+        int need = n;  // rank (from the top, 1-based) of the wanted key among the candidates
+        for (int pass = 0; pass < 8; ++pass) {
+            const int shift = 56 - 8 * pass;
+            uint32_t* h = hist + 256 * (pass & 1);
+            const bool cand = tid < N && (pass == 0 || (mine >> (shift + 8)) == (prefix >> (shift + 8)));
+            if (cand) atomicAdd(&h[(mine >> shift) & 255u], 1u);
+            __syncthreads();
+            if (wid == 0) {
+                uint32_t c[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) hh[u] = *reinterpret_cast<const uint4*>(&hi[j + 4 * u]);
+                for (int u = 0; u < 4; ++u) c[u] = h[4 * lane + u];
+                const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+                // keys in the bins above this lane's four: suffix sum over the lanes above
+                uint32_t above = 0, run = tot;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    rank += (hh[u].x > h) + (hh[u].y > h) + (hh[u].z > h) + (hh[u].w > h);
-                    eq += (hh[u].x == h) + (hh[u].y == h) + (hh[u].z == h) + (hh[u].w == h);
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const uint32_t o = __shfl_down(run, off, kWave);
+                    if (lane + off < kWave) run += o;
                 }
-            }
-            if (__any(tid < N && eq > 1)) {
-                int tie = 0;
-                for (int j = 0; j < N16; j += 2) {
-                    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(&keys[j]);
-                    tie += ((uint32_t)(kk.x >> 32) == h && kk.x > mine) + ((uint32_t)(kk.y >> 32) == h && kk.y > mine);
+                above = run - tot;
+#pragma unroll
+                for (int u = 3; u >= 0; --u) {
+                    if ((int)above < need && (int)(above + c[u]) >= need) {
+                        s_pick[0] = 4 * lane + u;
+                        s_pick[1] = need - (int)above;
+                    }
+                    above += c[u];
                 }
-                rank += tie;
+                // the other histogram is cleared for the next pass
+                uint32_t* hn = hist + 256 * ((pass + 1) & 1);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) hn[4 * lane + u] = 0;
             }
+            __syncthreads();
+            prefix |= (uint64_t)(uint32_t)s_pick[0] << shift;
+            need = s_pick[1];
         }
-        const bool keep = tid < N && rank < n;
+        // keys are unique: exactly n of them are >= the n-th largest
+        const bool keep = tid < N && mine >= prefix;
         const uint64_t bal = __ballot(keep);
         if (lane == 0) s_wave_kept[wid] = __popcll(bal);
         __syncthreads();
