@@ -81,19 +81,30 @@ __global__ __launch_bounds__(kChunkThreads) void expand_chunk_kernel(
     __syncthreads();
     if (wid != 0) return;
     // merge the four sorted wave lists by rank: a key's place in the chunk's list
-    // is the number of larger keys in the pool (keys are unique); lane l holds pool
-    // entries l and l + 64
+    // is the number of larger keys in the pool (keys are unique), the sum over the
+    // four lists (each sorted, best first, zero-padded) of how many of its entries
+    // are larger, found by a branch-free binary search whose steps read all four
+    // lists together.  Lane l holds pool entries l and l + 64.
     const int pool = kChunkWaves * k;  // <= 128
     const uint64_t c0 = lane < pool ? s_wl[lane / k][lane % k] : 0;
     const uint64_t c1 = lane + kWave < pool ? s_wl[(lane + kWave) / k][(lane + kWave) % k] : 0;
-    int r0 = 0, r1 = 0, nz = 0;
-    for (int w = 0; w < kChunkWaves; ++w)
-        for (int i = 0; i < k; ++i) {
-            const uint64_t x = s_wl[w][i];  // the same entry in every lane
-            r0 += x > c0;
-            r1 += x > c1;
-            nz += x != 0;
+    auto larger_in_pool = [&](uint64_t key) {
+        int lo[kChunkWaves];
+#pragma unroll
+        for (int w = 0; w < kChunkWaves; ++w) lo[w] = 0;
+#pragma unroll
+        for (int step = EAGLE_MAX_TOPK; step > 0; step >>= 1) {
+            if (step > k) continue;  // uniform
+#pragma unroll
+            for (int w = 0; w < kChunkWaves; ++w)
+                if (lo[w] + step <= k && s_wl[w][lo[w] + step - 1] > key) lo[w] += step;
         }
+        return lo[0] + lo[1] + lo[2] + lo[3];
+    };
+    static_assert(kChunkWaves == 4, "four wave lists");
+    const int r0 = c0 != 0 ? larger_in_pool(c0) : 2 * kWave;
+    const int r1 = c1 != 0 ? larger_in_pool(c1) : 2 * kWave;
+    const int nz = __popcll(__ballot(c0 != 0)) + __popcll(__ballot(c1 != 0));
     uint64_t* out = ckeys + (row * C + c) * (size_t)k;
     if (c0 != 0 && r0 < k) out[r0] = c0;
     if (c1 != 0 && r1 < k) out[r1] = c1;
