@@ -365,6 +365,9 @@ EDGE = [
     dict(dtype="f32", head_dim=128, n_q_heads=4, n_kv_heads=2, ctx=5, n=7),
     dict(batch=3, ctx_range=(2000, 9000), n_q_heads=40, n_kv_heads=40, n=60, depth=6, topk=10, m=10,
          vocab=4000, seed=9),                              # many units spread over many workgroups
+    dict(depth=4, topk=32, m=32, n=63, vocab=262144, batch=2, ctx=100, seed=13),  # largest vocabulary, top-k
+                                                           # and T; 3105 of the 4096 node slots
+    dict(batch=1024, ctx_range=(0, 60), n=8, seed=17),     # largest batch
 ]
 
 
