@@ -39,7 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attn_llama2_13b_traffic.json")
+# HBM counter records, one per workload they were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attn_{}_traffic.json")
 
 
 def attention_bytes_per_launch(w) -> int:
@@ -374,10 +375,11 @@ def main():
     tflops = flops_launch / (ms_per_launch * 1e-3) / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    traffic_file = TRAFFIC_FILE.format(w.name)
+    if os.path.exists(traffic_file):
         # counters taken on an older kernel source do not describe this one
         try:
-            rec = json.load(open(TRAFFIC_FILE))
+            rec = json.load(open(traffic_file))
             src = open(os.path.join(ROOT, rec["source"]), "rb").read()
             # the counters describe one workload and one kernel source
             if hashlib.sha256(src).hexdigest() == rec["source_sha256"] and rec.get("workload") == w.name:
