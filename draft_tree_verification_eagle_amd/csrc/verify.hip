@@ -68,7 +68,12 @@ constexpr int kRowThreads = 512;
 constexpr int kWgChunks = kRowThreads / 2;           // two threads per chunk
 constexpr int kRowChunks = kRowSplit * kWgChunks;    // 1024 chunks per row
 constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kRowBatch = 32;       // loads per thread in flight together
+constexpr int kRowBatch = 16;       // tokens per thread per step of the mass pass (<= 32)
+// float4 loads per thread in flight together in the maximum pass: a whole 32000-token
+// row in one step.  With the mass pass's step this keeps the kernel at 78 VGPRs,
+// three 512-thread workgroups per CU (a batch of many rows runs 3x as many at once)
+constexpr int kMaxBatch = 16;
+static_assert(kRowBatch <= 32, "one 32-bit window of the child mask per step");
 constexpr int kMaxChunkTokens = 256;  // ceil(EAGLE_MAX_VOCAB / 1024)
 static_assert((EAGLE_MAX_VOCAB + kRowChunks - 1) / kRowChunks <= kMaxChunkTokens, "chunk mask");
 static_assert(kRowSplit == 4, "RowStats keeps four partial rest masses");
@@ -105,15 +110,15 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     if (vec) {
         const int n4 = V >> 2;
         const float4* z4 = reinterpret_cast<const float4*>(z);
-        for (int j0 = 0; j0 < n4; j0 += kRowBatch * kRowThreads) {
-            float4 zr[kRowBatch];
+        for (int j0 = 0; j0 < n4; j0 += kMaxBatch * kRowThreads) {
+            float4 zr[kMaxBatch];
 #pragma unroll
-            for (int u = 0; u < kRowBatch; ++u) {
+            for (int u = 0; u < kMaxBatch; ++u) {
                 const int j = j0 + u * kRowThreads + tid;
                 zr[u] = j < n4 ? z4[j] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
 #pragma unroll
-            for (int u = 0; u < kRowBatch; ++u) {
+            for (int u = 0; u < kMaxBatch; ++u) {
                 const int j = j0 + u * kRowThreads + tid;
                 if (j < n4) {
                     const uint32_t t = 4u * (uint32_t)j;
