@@ -373,9 +373,12 @@ int orc_verify_greedy(int T, int V, const float* target, const int* flat_token,
 // fp64; children are tested in flat order; child c is accepted when
 //     u < p(tok c) / sum_{t not removed} p(t)
 // with u from Philox (slot = child index); a rejected child's token joins the
-// removed set.  When no child is accepted (or the row has none) the bonus
-// token is drawn from p with removed tokens zeroed: the smallest t whose
-// running sum exceeds u * (residual total), u from the bonus slot.
+// removed set.  A child whose token is already removed (an earlier sibling of
+// a caller-given static tree carried the same token) proposes a token of zero
+// residual mass, so its ratio is 0 and it is never accepted; it still uses its
+// slot.  When no child is accepted (or the row has none) the bonus token is
+// drawn from p with removed tokens zeroed: the smallest t whose running sum
+// exceeds u * (residual total), u from the bonus slot.
 //
 // trace [max_trace][4] receives (row, slot, u, ratio) per child test and
 // (row, -1, u, margin) for the bonus draw, where margin is the distance of
@@ -417,7 +420,7 @@ int orc_verify_sampled(int T, int V, const float* target, const int* flat_token,
                 double rest = 0.0;
                 for (int t = 0; t < V; ++t) if (!removed[t]) rest += p[t];
                 const int tok = flat_token[j];
-                const double ratio = p[tok] / rest;
+                const double ratio = removed[tok] ? 0.0 : p[tok] / rest;
                 const double u = uniform_for(seed, step, (uint32_t)seq, (uint32_t)cur, (uint32_t)slot);
                 put(cur, slot, u, ratio);
                 ++slot;

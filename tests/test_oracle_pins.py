@@ -432,7 +432,12 @@ def _ar_law(target, flat_token, flat_parent, temperature):
     law = {}
 
     def walk(row, prefix, prob):
-        kids = {int(flat_token[j]): j for j in range(T) if flat_parent[j] == row}
+        # a token carried by several siblings (possible in a caller-given static
+        # tree) leads into the first of them in flattened order
+        kids = {}
+        for j in range(T):
+            if flat_parent[j] == row:
+                kids.setdefault(int(flat_token[j]), j)
         for t in range(V):
             pt = prob * P[row, t]
             if pt == 0.0:
@@ -459,10 +464,13 @@ def _rule_law(target, flat_token, flat_parent, temperature):
         kids = [j for j in range(T) if flat_parent[j] == row]
         for j in kids:
             tok = int(flat_token[j])
-            acc = p[tok] / p.sum()
-            visit(j, prefix + (tok,), prob * acc)
+            acc = p[tok] / p.sum() if p[tok] > 0.0 else 0.0
+            if acc > 0.0:  # a token already removed at this row has no mass left
+                visit(j, prefix + (tok,), prob * acc)
             prob *= (1.0 - acc)
             p[tok] = 0.0
+        if p.sum() == 0.0:  # every token was a child and all were tested: no residual
+            return
         r = p / p.sum()
         for t in range(V):
             if r[t] > 0:
@@ -560,3 +568,162 @@ def test_sampled_trace_decisions_are_strict(orc):
                 assert u == orc.uniform(5, s, 0, int(row), int(slot))
                 accepted += int(u < ratio)
         assert accepted == al
+
+
+# ---------------------------------------------------------------------------
+# Sampled verification on caller-given static trees (EAGLE-2 page, opening
+# paragraphs: EAGLE and Medusa draft over a fixed tree), where a row may have up
+# to T - 1 children and siblings may carry the same token.  The rule must stay
+# lossless (EAGLE page abstract; CSDN page 1.2): a token already rejected at a
+# row has no residual mass left, so a later sibling carrying it is never
+# accepted.
+# ---------------------------------------------------------------------------
+def _static_trees():
+    """(name, flat_parent, flat_token, V, depth) of static trees with wide rows and
+    duplicate sibling tokens."""
+    out = []
+    # duplicate siblings at the root (rows 1, 2) and below row 1 (rows 4, 5); row 2's
+    # subtree can never be entered
+    out.append(("dup", np.array([-1, 0, 0, 0, 1, 1, 2, 3, 4], np.int32),
+                np.array([0, 2, 2, 4, 1, 1, 3, 2, 0], np.int32), 6, 4))
+    # a 63-child star with distinct tokens
+    out.append(("star63", np.array([-1] + [0] * 63, np.int32),
+                np.array([0] + list(range(5, 68)), np.int32), 72, 1))
+    # a 63-child star whose children carry only 12 distinct tokens
+    rng = np.random.default_rng(31)
+    out.append(("star63dup", np.array([-1] + [0] * 63, np.int32),
+                np.concatenate([[0], rng.integers(0, 12, 63)]).astype(np.int32), 16, 1))
+    # a wide random tree over a small vocabulary (many duplicates at every row)
+    par = [-1]
+    for i in range(1, 40):
+        par.append(0 if rng.random() < 0.4 else int(rng.integers(0, i)))
+    out.append(("wide40", np.array(par, np.int32), rng.integers(0, 7, 40).astype(np.int32), 7, 0))
+    # depth argument = the tree's own depth, so the walk is never cut short
+    res = []
+    for name, fp, ft, V, _ in out:
+        d = [0] * len(fp)
+        for i in range(1, len(fp)):
+            d[i] = d[fp[i]] + 1
+        res.append((name, fp, ft, V, max(d)))
+    return res
+
+
+def _static_target(flat_token, flat_parent, V, seed, boost=1.5):
+    rng = np.random.default_rng(seed)
+    T = len(flat_token)
+    target = rng.normal(0, 1.0, (T, V)).astype(np.float32)
+    for i in range(1, T):  # make acceptances common
+        if rng.random() < 0.5:
+            target[flat_parent[i], flat_token[i]] += boost
+    return target
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+@pytest.mark.parametrize("temp", [1.0, 0.7])
+def test_acceptance_rule_is_lossless_on_static_trees_closed_form(idx, temp):
+    """Exact enumeration: the accept/reject rule with removed tokens at zero mass
+    has the target's autoregressive law on trees with duplicate sibling tokens."""
+    name, fp, ft, V, depth = _static_trees()[idx]
+    target = _static_target(ft, fp, V, 40 + idx)
+    a = _ar_law(target, ft, fp, temp)
+    b = _rule_law(target, ft, fp, temp)
+    assert set(a) == set(b)
+    for key in a:
+        assert abs(a[key] - b[key]) < 1e-12
+
+
+def test_oracle_duplicate_sibling_never_accepted(orc):
+    """Every test of a sibling whose token an earlier sibling already carried has
+    ratio exactly 0, and such a row is never on an accepted path."""
+    for name, fp, ft, V, depth in _static_trees():
+        target = _static_target(ft, fp, V, 7)
+        T = len(ft)
+        dup = np.zeros(T, bool)
+        for j in range(1, T):
+            dup[j] = any(fp[i] == fp[j] and ft[i] == ft[j] for i in range(1, j))
+        assert dup.any() or name == "star63"
+        for s in range(300):
+            al, ap, ot, tr = orc.verify_sampled(target, ft, fp, depth, 1.0, 9, s, 0)
+            assert not any(dup[r] for r in ap[:al])
+            for row, slot, u, ratio in tr:
+                if slot < 0:
+                    continue
+                kids = [j for j in range(T) if fp[j] == int(row)]
+                j = kids[int(slot)]
+                if dup[j]:
+                    assert ratio == 0.0
+                else:
+                    assert ratio > 0.0
+
+
+def _mc_counts_lean(orc, target, ft, fp, depth, temp, n, seed):
+    """Emitted-sequence counts of n oracle draws (steps 0..n-1), calling the
+    oracle's C entry with preallocated buffers."""
+    import ctypes as C
+    L = orc.lib()
+    z = np.ascontiguousarray(target, np.float32); T, V = z.shape
+    ft = np.ascontiguousarray(ft, np.int32); fp = np.ascontiguousarray(fp, np.int32)
+    al = np.zeros(1, np.int32); ap = np.zeros(depth, np.int32); ot = np.zeros(depth + 1, np.int32)
+    tr = np.zeros((1, 4)); nt = np.zeros(1, np.int32)
+    ptr = lambda a: a.ctypes.data_as(C.c_void_p)
+    pz, pft, pfp, pal, pap, pot, ptr_, pnt = map(ptr, (z, ft, fp, al, ap, ot, tr, nt))
+    counts = {}
+    f = L.orc_verify_sampled
+    for s in range(n):
+        rc = f(T, V, pz, pft, pfp, depth, float(temp), seed, s, 0, pal, pap, pot, ptr_, 1, pnt)
+        assert rc == 0
+        key = tuple(int(x) for x in ot[: al[0] + 1])
+        counts[key] = counts.get(key, 0) + 1
+    return counts
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx,temp", [(0, 1.0), (1, 1.0), (2, 0.7), (3, 1.0)])
+def test_oracle_sampling_static_trees_monte_carlo_1e6(orc, idx, temp):
+    """10^6 oracle draws on static trees with wide rows and duplicate siblings
+    follow the target's autoregressive law (chi-square)."""
+    name, fp, ft, V, depth = _static_trees()[idx]
+    target = _static_target(ft, fp, V, 70 + idx)
+    law = _ar_law(target, ft, fp, temp)
+    n = 1_000_000
+    counts = _mc_counts_lean(orc, target, ft, fp, depth, temp, n, seed=4242 + idx)
+    assert _chi2_pvalue(counts, law, n) > 1e-3
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("seed,temp", [(0, 1.0), (1, 0.7)])
+def test_oracle_sampling_follows_target_law_monte_carlo_1e6(orc, seed, temp):
+    """The dynamic-tree Monte-Carlo pin at 10^6 draws."""
+    rng, flat = _small_tree(orc, 600 + seed, V=5, depth=3, k=2, m=2)
+    T = len(flat["flat_token"])
+    target = rng.normal(0, 1.0, (T, 5)).astype(np.float32)
+    for i in range(1, T):
+        if rng.random() < 0.5:
+            target[flat["flat_parent"][i], flat["flat_token"][i]] += 1.5
+    law = _ar_law(target, flat["flat_token"], flat["flat_parent"], temp)
+    n = 1_000_000
+    counts = _mc_counts_lean(orc, target, flat["flat_token"], flat["flat_parent"], 3, temp, n, seed=99 + seed)
+    assert _chi2_pvalue(counts, law, n) > 1e-3
+
+
+def test_oracle_greedy_static_trees_brute_force(orc):
+    """Greedy on static trees (wide rows, duplicate siblings): the accepted path is
+    the longest root path whose every token is its parent row's argmax, taking the
+    first sibling in flattened order where several carry it."""
+    for name, fp, ft, V, depth in _static_trees():
+        for seed in range(5):
+            target = _static_target(ft, fp, V, 300 + seed, boost=4.0)
+            T = len(ft)
+            # brute force: every root path, its greedy-consistent prefix
+            best_path = []
+            cur, path = 0, []
+            while len(path) < depth:
+                am = int(np.argmax(target[cur]))
+                kids = [j for j in range(T) if fp[j] == cur and ft[j] == am]
+                if not kids:
+                    break
+                cur = min(kids)
+                path.append(cur)
+            al, ap, ot = orc.verify_greedy(target, ft, fp, depth)
+            assert al == len(path) and list(ap[:al]) == path
+            assert ot[al] == int(np.argmax(target[path[-1] if path else 0]))
