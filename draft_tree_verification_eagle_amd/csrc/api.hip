@@ -36,6 +36,16 @@ int tree_limits(const eagle_tree_cfg* c, int32_t* cap) {
     return EAGLE_OK;
 }
 
+// Verification reads batch, vocab, depth and n only (the flattened tree may come
+// from a caller-given static tree, whose shape no topk / m describes).
+int verify_limits(const eagle_tree_cfg* c) {
+    if (!c || c->batch < 0 || c->vocab < 1 || c->depth < 1 || c->n < 0) return EAGLE_ERR_INVALID_ARG;
+    if (c->batch > EAGLE_MAX_BATCH || c->vocab > EAGLE_MAX_VOCAB || c->depth > 255 ||
+        c->n + 1 > EAGLE_MAX_TREE_ROWS)
+        return EAGLE_ERR_UNSUPPORTED;
+    return EAGLE_OK;
+}
+
 bool state_ok(const eagle_tree_state* s) {
     return s && s->token && s->parent && s->depth && s->value && s->frontier && s->n_nodes;
 }
@@ -145,8 +155,7 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
 }
 
 size_t eagle_verify_workspace(const eagle_tree_cfg* cfg) {
-    int32_t cap = 0;
-    if (tree_limits(cfg, &cap) != EAGLE_OK) return 0;
+    if (verify_limits(cfg) != EAGLE_OK) return 0;
     return eagle::verify_workspace_bytes(*cfg);
 }
 
@@ -154,8 +163,7 @@ int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const in
                  const int32_t* flat_parent, float temperature, uint64_t seed, uint64_t step,
                  int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
-    int32_t cap = 0;
-    const int st = tree_limits(cfg, &cap);
+    const int st = verify_limits(cfg);
     if (st != EAGLE_OK) return st;
     if (!(temperature >= 0.0f) || isinf(temperature)) return EAGLE_ERR_INVALID_ARG;
     if (cfg->batch == 0) return EAGLE_OK;

@@ -14,7 +14,11 @@
 // K6 (four workgroups per row) computes argmax, row max and, for sampling, the fp64
 // masses exp((z - zmax) / temperature) of every child token plus the fp64 mass of
 // all other tokens, summed directly (never as 1 - sum of removed), and the
-// fixed-point mass of each of 1024 contiguous token chunks.  K7 (one workgroup
+// fixed-point mass of each of 1024 contiguous token chunks.  A row may have up to
+// T - 1 children (caller-given static trees), and siblings may carry the same
+// token: a token already rejected at a row has no residual mass, so a later
+// sibling carrying it has acceptance probability 0, and each removed token's
+// mass leaves the residual once.  K7 (one workgroup
 // per sequence) walks the tree with Philox4x32-10 uniforms and draws the bonus
 // token by inverse CDF: a block-wide prefix sum over the final row's chunk masses
 // (minus the removed tokens) finds the chunk holding u * total, and one wave
@@ -26,7 +30,9 @@
 
 namespace eagle {
 
-constexpr int kKids = EAGLE_MAX_TOPK;
+// children of one row: every other row of the tree at most
+constexpr int kKids = EAGLE_MAX_TREE_ROWS;
+static_assert(kKids <= kWave, "one wave holds a row's children, lane = row");
 
 // Token mass in fixed point: masses are <= 1 (the row maximum has mass 1); with
 // 2^s, s = 63 - ceil(log2 V), a row total stays below 2^63, so prefix sums are
@@ -39,15 +45,13 @@ __host__ __device__ inline int fixed_shift(int V) {
 }
 __device__ __forceinline__ uint64_t fixed_mass(double e, double scale) { return (uint64_t)(e * scale); }
 
-// Per-row statistics in the workspace.
+// Per-row statistics in the workspace.  Every row but the root has exactly one
+// parent, so a child's mass in its parent's row is kept with the child.
 struct RowStats {
-    double rest[4];     // mass of tokens that are not children of the row, per quarter of its chunks
-    double kid_e[kKids];  // mass of each child's token, flattened order
-    int32_t kid_row[kKids];
+    double rest[4];  // mass of tokens that are not children of the row, per quarter of its chunks
+    double e_kid;    // mass of this row's token in its parent row (sampled mode; unused for the root)
     float zmax;
     int32_t argmax;
-    int32_t n_kids;
-    int32_t pad;
 };
 
 // ---------------------------------------------------------------------------
@@ -60,8 +64,9 @@ struct RowStats {
 // chunk, re-read from L2), with a 256-bit mask of the row's children in the chunk: it
 // stores each chunk's fixed-point mass (children included) for the bonus draw and
 // the fp64 mass of the non-child tokens of its quarter.  Workgroup 0 also writes
-// the children, their fp64 masses, the argmax and the maximum.  Wave 0 of each
-// workgroup finds the children with one ballot (flattened order = lane order).
+// the argmax and the maximum, and each child's fp64 mass into the child's own
+// statistics.  Wave 0 of each workgroup finds the children with one ballot
+// (flattened order = lane order).
 // ---------------------------------------------------------------------------
 constexpr int kRowSplit = 4;
 constexpr int kRowThreads = 512;
@@ -98,11 +103,11 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         const bool kid = lane < T && flat_parent[(size_t)b * T + lane] == i;
         const uint64_t bal = __ballot(kid);
         const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-        if (kid && pos < kKids) {
+        if (kid) {  // pos < 64 = kKids
             s_kid_row[pos] = lane;
             s_kid_tok[pos] = flat_token[(size_t)b * T + lane];
         }
-        if (lane == 0) s_nk = __popcll(bal) < kKids ? __popcll(bal) : kKids;
+        if (lane == 0) s_nk = __popcll(bal);
     }
     // maximum and argmax over the whole row: (logit, ~token) keys, order-free
     uint64_t best = 0;
@@ -220,15 +225,16 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         if (half == 0) chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
         s = block_sum_f64(s, s_red);
         if (tid == 0) out->rest[q] = s;
+        // the same expression as the chunk masses' (x / 1 == x exactly), so the bonus
+        // draw can take a removed token's fixed-point mass out of its chunk exactly
         if (q == 0 && tid < nk)
-            out->kid_e[tid] = exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
+            stats[(size_t)b * T + s_kid_row[tid]].e_kid =
+                exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
     }
     if (q != 0) return;
-    if (tid < nk) out->kid_row[tid] = s_kid_row[tid];
     if (tid == 0) {
         out->zmax = zmax;
         out->argmax = amax;
-        out->n_kids = nk;
     }
 }
 
@@ -268,15 +274,19 @@ __device__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* s_wave, uint6
 
 __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
     const float* __restrict__ target, int T, int V, int depth, const int32_t* __restrict__ flat_token,
-    float temperature, uint64_t seed, uint64_t step, const RowStats* __restrict__ stats,
+    const int32_t* __restrict__ flat_parent, float temperature, uint64_t seed, uint64_t step,
+    const RowStats* __restrict__ stats,
     const uint64_t* __restrict__ chunk_mass, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ accept_path, int32_t* __restrict__ out_tokens) {
     __shared__ RowStats s_rs[EAGLE_MAX_TREE_ROWS];
     __shared__ int32_t s_tok[EAGLE_MAX_TREE_ROWS];
+    __shared__ int32_t s_par[EAGLE_MAX_TREE_ROWS];
+    __shared__ int32_t s_first[EAGLE_MAX_TREE_ROWS];  // 1: no earlier sibling carries the row's token
     __shared__ int32_t s_path[kMaxDepth];      // depth <= 255: accepted rows, -1 padded
     __shared__ int32_t s_out[kMaxDepth + 1];   // accepted tokens then the bonus, -1 padded
     __shared__ int s_bonus_row, s_len;
-    __shared__ int32_t s_removed[kKids];
+    __shared__ int32_t s_removed[kKids];   // distinct tokens rejected at the final row
+    __shared__ double s_removed_e[kKids];  // and their fp64 masses
     __shared__ int s_n_removed;
     __shared__ uint64_t s_wave[kWalkThreads / kWave];
     __shared__ int s_hit_chunk;
@@ -291,37 +301,56 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
         uint64_t* dst = (uint64_t*)s_rs;
         const int words = T * (int)(sizeof(RowStats) / 8);
         for (int w = tid; w < words; w += kWalkThreads) dst[w] = src[w];
-        if (tid < T) s_tok[tid] = flat_token[(size_t)b * T + tid];
+        if (tid < T) {
+            s_tok[tid] = flat_token[(size_t)b * T + tid];
+            s_par[tid] = flat_parent[(size_t)b * T + tid];
+        }
         if (tid < depth) s_path[tid] = -1;
         if (tid <= depth) s_out[tid] = -1;
     }
     __syncthreads();
+    if (tid < T) {
+        int first = 1;
+        for (int j = 1; j < tid; ++j)
+            if (s_par[j] == s_par[tid] && s_tok[j] == s_tok[tid]) first = 0;
+        s_first[tid] = first;
+    }
+    __syncthreads();
 
-    // The walk, by wave 0: lane c evaluates child c of the current row.  The
-    // sequential rule takes the first child (flattened order) whose test passes,
-    // and child c's test depends only on c (the children before it are the ones
-    // already removed), so the lowest set bit of the ballot is that child.
+    // The walk, by wave 0: lane j evaluates row j when it is a child of the
+    // current row; its slot is its index among the row's children (flattened
+    // order).  The sequential rule takes the first child whose test passes, and
+    // child c's test depends only on c (the children before it are the ones
+    // already rejected), so the lowest set bit of the ballot is that child.  The
+    // tokens not yet rejected when child c is tested are the non-children (mass
+    // `rest`) and the tokens whose first carrier among the children is c or later;
+    // a child whose token an earlier sibling carried has probability 0.
     if (tid < kWave) {
         int cur = 0, len = 0;
         while (true) {
             const RowStats& R = s_rs[cur];
-            const int nk = R.n_kids;
+            const bool is_kid = lane < T && s_par[lane] == cur;
+            const uint64_t kids = __ballot(is_kid);
             int next = -1;
-            if (len < depth && nk > 0) {
+            if (len < depth && kids) {
                 bool pass = false;
-                if (lane < nk) {
+                if (is_kid) {
                     if (!sampled) {
-                        pass = s_tok[R.kid_row[lane]] == R.argmax;
+                        pass = s_tok[lane] == R.argmax;
                     } else {
                         double denom = ((R.rest[0] + R.rest[1]) + R.rest[2]) + R.rest[3];
-                        for (int c = lane; c < nk; ++c) denom += R.kid_e[c];
-                        const double ratio = R.kid_e[lane] / denom;
-                        const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)lane);
+                        for (uint64_t m = kids >> lane; m; m &= m - 1) {
+                            const int j = lane + __ffsll((unsigned long long)m) - 1;
+                            if (s_first[j]) denom += s_rs[j].e_kid;
+                        }
+                        const double ratio = s_first[lane] ? s_rs[lane].e_kid / denom : 0.0;
+                        const int slot = __popcll(kids & ((1ull << lane) - 1ull));
+                        const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)slot);
                         pass = u < ratio;
                     }
                 }
                 const uint64_t bal = __ballot(pass);
-                if (bal) next = R.kid_row[__ffsll((unsigned long long)bal) - 1];
+                if (bal) next = __ffsll((unsigned long long)bal) - 1;
             }
             if (next >= 0) {
                 if (lane == 0) {
@@ -332,14 +361,21 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                 cur = next;
                 continue;
             }
+            // every child of the final row was tested and rejected (none when it is a
+            // leaf, or when the path has reached the depth limit): its distinct tokens
+            const bool rem = len < depth && is_kid && s_first[lane];
+            const uint64_t rbal = __ballot(rem);
+            if (rem) {
+                const int c = __popcll(rbal & ((1ull << lane) - 1ull));
+                s_removed[c] = s_tok[lane];
+                s_removed_e[c] = s_rs[lane].e_kid;
+            }
             if (lane == 0) {
                 if (!sampled) s_out[len] = R.argmax;
                 s_bonus_row = cur;
                 s_len = len;
-                // every child of the final row was tested and rejected (none when it is a leaf)
-                s_n_removed = (len < depth) ? nk : 0;
+                s_n_removed = __popcll(rbal);
             }
-            if (len < depth && lane < nk) s_removed[lane] = s_tok[R.kid_row[lane]];
             break;
         }
     }
@@ -363,8 +399,8 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
         const int c0 = min(V, tid * ch), c1 = min(V, c0 + ch);
         uint64_t cs = chunk_mass[((size_t)b * T + row) * kWalkThreads + tid];
         for (int c = 0; c < nrem; ++c) {
-            const int tok = s_removed[c];  // child c's token; its mass is R.kid_e[c]
-            if (tok >= c0 && tok < c1) cs -= fixed_mass(R.kid_e[c], fscale);
+            const int tok = s_removed[c];  // distinct tokens: each leaves its chunk once
+            if (tok >= c0 && tok < c1) cs -= fixed_mass(s_removed_e[c], fscale);
         }
         const Philox4x32 word = philox4x32_10(Philox4x32{kBonusSlot, (uint32_t)row, (uint32_t)b, (uint32_t)step},
                                               (uint32_t)seed, (uint32_t)(seed >> 32));
@@ -443,7 +479,7 @@ hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     verify_walk_kernel<<<cfg.batch, kWalkThreads, 0, stream>>>(
-        target, T, cfg.vocab, cfg.depth, flat_token, temperature, seed, step, stats, chunk_mass,
+        target, T, cfg.vocab, cfg.depth, flat_token, flat_parent, temperature, seed, step, stats, chunk_mass,
         accept_len, accept_path, out_tokens);
     return hipGetLastError();
 }

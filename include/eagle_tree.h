@@ -194,22 +194,29 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
 
 /* Verify (CSDN page 1.1/1.2, EAGLE page: the emitted tokens must follow the
  * target's own distribution).  target_logits [batch][T][vocab] fp32: row i is the
- * target's next-token logits after flattened row i.
+ * target's next-token logits after flattened row i.  The children of a row are
+ * the rows whose flat_parent it is, in flattened order; a row may have up to
+ * T - 1 of them (static trees), and siblings may carry the same token.
  *   temperature == 0: greedy -- starting at the root row, accept the child whose
  *     token is the row's argmax (lowest id on ties) while one exists; the final
  *     row's argmax is the bonus token.
  *   temperature > 0: sampled -- p = softmax(z / temperature); the children of the
  *     current row are tested in flattened order, child c accepted iff
  *     u < p(tok c) / (mass of the tokens not yet rejected at this row); a rejected
- *     child's token is removed.  With no acceptance (or no child) the bonus token
+ *     child's token is removed, so a later sibling carrying the same token is
+ *     never accepted.  With no acceptance (or no child) the bonus token
  *     is the smallest t whose running residual mass exceeds u * (residual total).
  *     u = top 24 bits / 2^24 of word 0 of Philox4x32-10 (Salmon et al., SC'11) with
  *     key (seed low, seed high) and counter (slot, row, sequence, step low 32
  *     bits); slot = child index, 0xFFFFFFFF for the bonus draw.
  * Outputs: accept_len [batch] (0..depth), accept_path [batch][depth] (flattened
  * rows, -1 padded), out_tokens [batch][depth + 1] (accepted tokens then the bonus,
- * -1 padded).  flat_token / flat_parent from eagle_tree_mask.  Negative or NaN
- * temperature is EAGLE_ERR_INVALID_ARG.  Workspace: eagle_verify_workspace bytes. */
+ * -1 padded).  flat_token / flat_parent from eagle_tree_mask (or the caller's
+ * static tree: flat_parent[b][0] = -1, 0 <= flat_parent[b][i] < i otherwise).
+ * Only batch, vocab, depth and n of cfg are read (T = n + 1; topk and m are
+ * ignored); n + 1 > EAGLE_MAX_TREE_ROWS, vocab > EAGLE_MAX_VOCAB or depth > 255 is
+ * EAGLE_ERR_UNSUPPORTED.  Negative or NaN temperature is EAGLE_ERR_INVALID_ARG.
+ * Workspace: eagle_verify_workspace bytes. */
 size_t eagle_verify_workspace(const eagle_tree_cfg* cfg);
 
 int eagle_verify(const eagle_tree_cfg* cfg, const float* target_logits, const int32_t* flat_token,

@@ -14,11 +14,12 @@ import numpy as np
 import pytest
 import torch
 
+from parity_helpers import first_divergence_exempt
+
 pytestmark = pytest.mark.gpu
 
 ATOL_BF16 = 2e-2
 ATOL_F32 = 1e-5
-EXEMPT = 1e-6
 
 
 @pytest.fixture(scope="module")
@@ -55,7 +56,10 @@ def mask_words(mask_tt):
 
 
 def compare_trees(vs, trees):
-    """Bit-exact tree comparison; returns the number of sequences compared exactly."""
+    """Bit-exact tree comparison; returns the number of sequences compared in full.
+    A sequence whose draft rows include one the oracle flags as an fp64 rounding
+    hazard (its fp32 log-normaliser may round either way) is compared bit for bit
+    up to that row: every node created from an earlier draft row."""
     st = vs.state
     tok = st.token.cpu().numpy(); par = st.parent.cpu().numpy(); dep = st.depth.cpu().numpy()
     val = st.value.cpu().numpy(); nn = st.n_nodes.cpu().numpy()
@@ -74,11 +78,19 @@ def compare_trees(vs, trees):
         same = same and np.array_equal(ft[b], flat["flat_token"]) and np.array_equal(fp[b], flat["flat_parent"])
         same = same and np.array_equal(fd[b], flat["flat_depth"]) and np.array_equal(pos[b], flat["position"])
         same = same and np.array_equal(mk[b], mask_words(flat["mask"]))
-        if not same:
-            assert tree["row_hazard"].any(), f"sequence {b}: GPU tree differs from the oracle with no rounding hazard"
-            say(f"sequence {b}: tree differs on a flagged fp64 rounding hazard (allowed)")
-        else:
+        haz = np.nonzero(tree["row_hazard"])[0]
+        if haz.size == 0:
+            assert same, f"sequence {b}: GPU tree differs from the oracle"
             exact += 1
+            continue
+        # draft row r (layer-major, frontier order) creates nodes 1 + topk * r ... 1 + topk * (r + 1) - 1
+        upto = min(n, 1 + vs.w.topk * int(haz[0]))
+        assert (np.array_equal(tok[b, :upto], tree["token"][:upto]) and np.array_equal(par[b, :upto], tree["parent"][:upto])
+                and np.array_equal(dep[b, :upto], tree["depth"][:upto])
+                and np.array_equal(val[b, :upto].view(np.uint32), tree["value"][:upto].view(np.uint32))), \
+            f"sequence {b}: GPU tree differs from the oracle before the first flagged draft row {haz[0]}"
+        say(f"sequence {b}: compared up to the first flagged draft row {haz[0]} ({upto} nodes); same after it: {same}")
+        exact += int(same)
     return exact
 
 
@@ -115,7 +127,7 @@ def attention_check(orc, vs, trees, layer, n_pairs_per_seq=None, seqs=None, atol
             lerr = max(abs(lse_gpu[b, i, h] - lse[j]) for j, (i, h) in enumerate(sel)) if lse_gpu is not None else 0.0
         assert np.isfinite(got).all()
         assert err <= atol, f"seq {b} layer {layer}: max |o - oracle| = {err}"
-        assert lerr <= max(atol, 1e-4), f"seq {b} layer {layer}: max |lse - oracle| = {lerr}"
+        assert lerr <= atol, f"seq {b} layer {layer}: max |lse - oracle| = {lerr}"
         worst = max(worst, err)
     return worst
 
@@ -145,11 +157,12 @@ def verify_check(orc, vs, w, target, ft, fp, temperature, seed, steps):
             same = al[b] == l and np.array_equal(ap[b], p) and np.array_equal(ot[b], o)
             if not same:
                 assert temperature > 0.0, f"greedy mismatch seq {b} step {s}"
-                near = [row for row in tr if (row[1] >= 0 and abs(row[2] - row[3]) < EXEMPT) or
-                        (row[1] < 0 and row[3] < EXEMPT)]
-                assert near, f"sampled mismatch seq {b} step {s} with no decision within {EXEMPT}"
+                assert first_divergence_exempt(tr, fp[b], al[b], ap[b], l, p), \
+                    f"sampled mismatch seq {b} step {s}: the first differing decision is not within 1e-6"
                 exempt += 1
             taus.append(int(l) + 1)
+    # exemptions are rare: each needs a uniform within 1e-6 of its threshold
+    assert exempt <= max(1, (w.batch * len(steps)) // 1000), f"{exempt} exempt sequences"
     return exempt, float(np.mean(taus))
 
 
@@ -215,16 +228,18 @@ def test_attention_parity_7b_layer_all_outputs(lib, orc):
     same_without_host_lengths(eb, vs)
 
 
-def test_attention_parity_13b_sampled_layers(lib, orc):
+def test_attention_parity_13b_layers(lib, orc):
     eb, stepm, wl = lib
     w = wl.CONFIGS["llama2_13b"]
-    say("[attention parity] llama2_13b, 2 layers at full size, sampled outputs")
+    say("[attention parity] llama2_13b at full size: every output of layer 0, sampled outputs of layer 1")
     vs = stepm.VerifyStep(w, layers=2)
     vs.tree(); vs.attention()
     torch.cuda.synchronize()
     trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
+    worst = attention_check(orc, vs, trees, 0, None)
+    say(f"  layer 0, all 61 x 40 (row, head) outputs: worst |o - oracle| = {worst:.2e}")
+    attention_check(orc, vs, trees, 1, 120, seed=1)
     for layer in range(2):
-        attention_check(orc, vs, trees, layer, 120, seed=layer)
         o = vs.attn[layer]["o"]
         assert torch.isfinite(o.float()).all()
     # repeated launches reuse the workspace: identical bits
@@ -234,15 +249,16 @@ def test_attention_parity_13b_sampled_layers(lib, orc):
     assert torch.equal(o0, vs.attn[0]["o"])
 
 
-def test_attention_parity_70b_gqa_sampled(lib, orc):
+def test_attention_parity_70b_gqa_layer(lib, orc):
     eb, stepm, wl = lib
     w = wl.CONFIGS["llama2_70b_gqa"]
-    say("[attention parity] llama2_70b_gqa, 1 layer at full size, sampled outputs")
+    say("[attention parity] llama2_70b_gqa, 1 layer at full size, every output")
     vs = stepm.VerifyStep(w, layers=1)
     vs.tree(); vs.attention()
     torch.cuda.synchronize()
     trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
-    attention_check(orc, vs, trees, 0, 160)
+    worst = attention_check(orc, vs, trees, 0, None)
+    say(f"  all 61 x 64 (row, head) outputs: worst |o - oracle| = {worst:.2e}")
 
 
 @pytest.mark.skip(reason="faulted the GPU (memory aperture violation) with an earlier bf16 attention kernel "
