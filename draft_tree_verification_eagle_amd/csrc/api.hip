@@ -154,6 +154,18 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
     return from_hip(eagle::launch_attention(*desc, q, k_cache, v_cache, mask, o, lse, workspace, stream));
 }
 
+int eagle_tree_attention_noalloc(const eagle_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                                 hipStream_t stream) {
+    const int st = attn_desc_check(desc);
+    if (st != EAGLE_OK) return st;
+    if (desc->batch == 0) return EAGLE_OK;
+    if (!q || !k_cache || !v_cache || !mask || !o || !desc->ctx_len || !desc->kv_row_off)
+        return EAGLE_ERR_INVALID_ARG;
+    if (eagle::attention_workspace_bytes(*desc) > (size_t)EAGLE_NOALLOC_SCRATCH_BYTES) return EAGLE_ERR_WORKSPACE;
+    return from_hip(eagle::launch_attention_noalloc(*desc, q, k_cache, v_cache, mask, o, lse, stream));
+}
+
 size_t eagle_verify_workspace(const eagle_tree_cfg* cfg) {
     if (verify_limits(cfg) != EAGLE_OK) return 0;
     return eagle::verify_workspace_bytes(*cfg);

@@ -35,6 +35,13 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
                             const void* v, const uint64_t* mask, void* o, float* lse,
                             void* workspace, hipStream_t stream);
 
+// The same launch with the partials in the library's per-device array of
+// EAGLE_NOALLOC_SCRATCH_BYTES (no caller workspace); the caller has checked the
+// size against the array's.
+hipError_t launch_attention_noalloc(const eagle_attn_desc& d, const void* q, const void* k,
+                                    const void* v, const uint64_t* mask, void* o, float* lse,
+                                    hipStream_t stream);
+
 size_t verify_workspace_bytes(const eagle_tree_cfg& cfg);
 hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const int32_t* flat_token,
                          const int32_t* flat_parent, float temperature, uint64_t seed,

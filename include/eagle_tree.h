@@ -192,6 +192,24 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
                          const void* v_cache, const uint64_t* mask, void* o, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Tree attention without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same operation, arguments, layouts, kernels and results
+ * (bit for bit) as eagle_tree_attention; the split-KV partials live in a
+ * file-scope device array of EAGLE_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends (its address is taken once per
+ * device, on the first call with that device current; `stream` must belong to
+ * the current device).  The call allocates and frees nothing.  A shape whose
+ * eagle_tree_attention_workspace exceeds EAGLE_NOALLOC_SCRATCH_BYTES is
+ * EAGLE_ERR_WORKSPACE (nothing launched); other checks as eagle_tree_attention.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race; order them on one stream. */
+#define EAGLE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int eagle_tree_attention_noalloc(const eagle_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                                 hipStream_t stream);
+
 /* Verify (CSDN page 1.1/1.2, EAGLE page: the emitted tokens must follow the
  * target's own distribution).  target_logits [batch][T][vocab] fp32: row i is the
  * target's next-token logits after flattened row i.  The children of a row are

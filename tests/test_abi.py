@@ -331,3 +331,24 @@ def test_kv_gather_validation(eb):
     assert call(sv=None) == eb.EAGLE_ERR_INVALID_ARG
     assert call(k=0x4008) == eb.EAGLE_ERR_INVALID_ARG
     assert call(ctx=None) == eb.EAGLE_ERR_INVALID_ARG
+
+
+def test_noalloc_attention_validation(eb):
+    """The no-workspace attention call rejects a shape whose partials exceed its
+    array, and bad arguments, before any HIP call."""
+    L = eb.lib()
+
+    class Dev:
+        def data_ptr(self):
+            return 0x1000
+
+    f = 0x1000
+    d = eb.make_attn_desc(eb.EAGLE_BF16, 1, 64, 1024, 1024, 128, Dev(), Dev(), 4096)
+    assert eb.eagle_tree_attention_workspace(d) > (16 << 20)
+    assert L.eagle_tree_attention_noalloc(C.byref(d), f, f, f, f, f, None, None) == eb.EAGLE_ERR_WORKSPACE
+    d2 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 128, Dev(), Dev(), 4096)
+    assert L.eagle_tree_attention_noalloc(C.byref(d2), None, f, f, f, f, None, None) == eb.EAGLE_ERR_INVALID_ARG
+    d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 96, Dev(), Dev(), 4096)
+    assert L.eagle_tree_attention_noalloc(C.byref(d3), f, f, f, f, f, None, None) == eb.EAGLE_ERR_UNSUPPORTED
+    d4 = eb.make_attn_desc(eb.EAGLE_BF16, 0, 16, 8, 8, 128, Dev(), Dev(), 4096)
+    assert L.eagle_tree_attention_noalloc(C.byref(d4), f, f, f, f, f, None, None) == eb.EAGLE_OK  # empty batch
