@@ -6,15 +6,19 @@
 // own ancestors only (the It / is / a / has example), so one target pass verifies
 // every branch at once.
 //
-// BF16 path (head_dim 128): per sequence, a main kernel and a merge kernel.
-//  * Work unit = (KV head, group of 64 packed query rows); the packed rows of a KV
-//    head are its G = Hq/Hkv query heads x T tree rows.  The 64-key tiles of all
-//    units (ctx + T keys each) form one list, split over 256 workgroups, one per
-//    CU, on tile boundaries and weighted so that a workgroup spanning two units
-//    (two segments to merge and write) takes fewer tiles.  Workgroup index ->
-//    list position is XCD-aware (blockIdx % 8 picks the XCD): each XCD takes one
-//    contiguous run of stretches, so the units that share K/V rows (GQA) read
-//    them through one L2, and the partials of a unit land mostly in one L2.
+// BF16 path (head_dim 128): a main kernel and a merge kernel per launch of up to
+// 256 sequences (the work plan is in attn_plan.hpp).
+//  * Work unit = (sequence, KV head, group of 64 packed query rows); the packed
+//    rows of a KV head are its G = Hq/Hkv query heads x T tree rows.  The 64-key
+//    tiles of all units of all the launch's sequences (ctx_b + T keys each) form
+//    one list, split over 256 workgroups, one per CU, on tile boundaries and
+//    weighted so that a workgroup spanning two units (two segments to merge and
+//    write) takes fewer tiles; a workgroup walks from one sequence's units into the
+//    next, so short sequences share the GPU instead of each filling it alone.
+//    Workgroup index -> list position is XCD-aware (blockIdx % 8 picks the XCD):
+//    each XCD takes one contiguous run of stretches, so the units that share K/V
+//    rows (GQA) read them through one L2, and the partials of a unit land mostly
+//    in one L2.
 //  * Eight waves per workgroup: four compute, four only load.  K and V stream HBM ->
 //    LDS by direct 16-byte global_load_lds (no register staging), four stages
 //    deep, issued and waited for by the loader waves alone (each issues a quarter
@@ -46,6 +50,7 @@
 //    workgroup ever waits for another; each unit is merged on the XCD whose
 //    stretches hold the middle of it, where most of its partials are still in
 //    L2 (written back, not dropped, when the main kernel ends).
+#include "attn_plan.hpp"
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -65,8 +70,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_ADDR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int kD = 128;
-constexpr int kTileKeys = 64;
-constexpr int kUnitRows = 64;
+constexpr int kTileKeys = plan::kTileKeys;
+constexpr int kUnitRows = plan::kUnitRows;
 constexpr int kComputeWaves = 4;                     // 2 query halves x 2 key halves
 #ifndef EAGLE_LOADERS
 #define EAGLE_LOADERS 4
@@ -81,13 +86,6 @@ static_assert(kGridWG % 8 == 0, "workgroups are dealt to the 8 XCDs in turn");
 // the XCDs in turn).  Of n stretches, XCD x takes [xcd_first(x, n),
 // xcd_first(x + 1, n)): one contiguous run each, sizes differing by at most one.
 __host__ __device__ inline int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
-// Unit u's middle lies at fraction (u + 1/2) / units of the cost line, which
-// XCD floor((8u + 4) / units) holds; XCD x merges units [merge_unit_first(x),
-// merge_unit_first(x + 1)), at most ceil(units / 8) of them.
-__host__ __device__ inline int merge_unit_first(int x, int units) {
-    const int t = x * units - 4;
-    return t <= 0 ? 0 : (t + 7) >> 3;
-}
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kTileKeys * kRowBytes;    // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;          // K tile | V tile
@@ -187,115 +185,62 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One sequence.  Pointers are already offset to the sequence.
+using plan::Pos;
+using plan::Split;
+using plan::Tile;
+using plan::Walker;
+
+// One launch: up to plan::kMaxSeqs sequences.  Pointers are offset to the
+// launch's first sequence.
+constexpr int kArgSeqs = 32;  // up to this batch, a host-computed plan rides in the arguments
+
+// The per-sequence table computed on the host when it knows the context lengths
+// (read by the kernel with scalar loads of its arguments; for one sequence it is a
+// single cache line, loaded with the other arguments), so the kernel starts with
+// no scan and no dependent memory read.
+struct HostPlan {
+    int32_t S[kArgSeqs];
+    int64_t row0[kArgSeqs];
+    uint32_t cost0[kArgSeqs + 1];
+    int64_t key0[kArgSeqs + 1];
+};
+
 struct AttnArgs {
-    const __bf16* q;           // [T][Hq][D]
-    const __bf16* k;           // cache base; the sequence's rows start at *kv_row_off
+    const __bf16* q;           // [B][T][Hq][D]
+    const __bf16* k;           // cache base [Hkv][kv_rows_total][D]; sequence b's rows start at its row0
     const __bf16* v;
-    const uint64_t* mask;      // [T]
-    __bf16* o;                 // [T][Hq][D]
-    float* lse;                // [T][Hq] or null
-    const int32_t* ctx_len;    // [1], read when ctx_h < 0
-    const int64_t* kv_row_off; // [1], read when ctx_h < 0
-    _Float16* part_o;          // [slots][64][128], normalised rows
-    float* part_ml;            // [slots][2][64]: row reference max (base 2), row sum
+    const uint64_t* mask;      // [B][T]
+    __bf16* o;                 // [B][T][Hq][D]
+    float* lse;                // [B][T][Hq] or null
+    const int32_t* ctx_len;    // [B], read when there is no host plan
+    const int64_t* kv_row_off; // [B]
+    _Float16* part_o;          // [2 * grid][64][128]: normalised partial rows of split units
+    uint64_t* part_ml;         // [2 * grid][64]: per row (reference max (base 2), row sum) as two fp32
     int64_t kv_rows_total;
-    int T, Hq, Hkv, G, RG;
+    int B, T, Hq, Hkv, G, RG;
     float scale_log2;
-    int ctx_h;                 // the sequence's context length from the host, or -1
-    int64_t row0_h;            // its first cache row from the host (when ctx_h >= 0)
+    HostPlan hp;               // kHostLen only
 };
 
-// Work split.  Each unit's keys form nt = ceil(S / 64) tiles; the tiles are laid
-// on a cost line, unit after unit, each tile 4 cost steps long and each unit
-// preceded by kSegCost4 steps that stand for the fixed work of a segment (its
-// key-half merge and its output).  The line is cut into nwg equal stretches and a
-// workgroup takes the tiles that start in its stretch, so stretches end on tile
-// boundaries and a workgroup that spans two units takes fewer tiles.  Every
-// stretch is at least one tile long, so one that lies inside a unit's tiles holds
-// a tile start; one that falls wholly in the steps before a unit's first tile is
-// empty (its workgroup exits).  The workgroups holding a unit's tiles are
-// consecutive, none of them empty.
-constexpr int kSegCost4 = 16;
-// All in 32-bit steps: the host checks that the cost line fits in 31 bits.
-struct Split {
-    uint32_t W;      // cost steps per unit
-    uint32_t Wt;     // cost steps in all
-    uint32_t q, r;   // Wt = q * nwg + r
-    int nt;          // tiles per unit
-    int nwg;         // workgroups that take part
+// The per-sequence table, as the plan functions read it: from the launch
+// arguments (host plan) or from LDS (built by the kernel).
+struct ArgTab {
+    const HostPlan* hp;
+    __host__ __device__ int S(int b) const { return hp->S[b]; }
+    __host__ __device__ int64_t row0(int b) const { return hp->row0[b]; }
+    __host__ __device__ uint32_t cost0(int b) const { return hp->cost0[b]; }
+    __host__ __device__ int64_t key0(int b) const { return hp->key0[b]; }
 };
-__host__ __device__ inline Split make_split(int S, int units, int grid) {
-    Split sp;
-    sp.nt = (S + kTileKeys - 1) / kTileKeys;
-    sp.W = 4u * (uint32_t)sp.nt + kSegCost4;
-    sp.Wt = (uint32_t)units * sp.W;
-    const uint32_t most = sp.Wt / 4;
-    sp.nwg = most < (uint32_t)grid ? (most > 0 ? (int)most : 1) : grid;
-    sp.q = sp.Wt / (uint32_t)sp.nwg;
-    sp.r = sp.Wt - sp.q * (uint32_t)sp.nwg;
-    return sp;
-}
-// First cost step of stretch v: floor(Wt * v / nwg).
-__host__ __device__ inline uint32_t stretch_start(const Split& sp, int v) {
-    return sp.q * (uint32_t)v + (sp.r * (uint32_t)v) / (uint32_t)sp.nwg;
-}
-// First tile (unit, tile) starting at or after cost step p; (units, 0) past the last.
-struct TilePos {
-    int unit, tile;
+struct LdsTab {
+    const int32_t* s;
+    const int64_t* r;
+    const uint32_t* c;
+    const int64_t* k;
+    __device__ int S(int b) const { return s[b]; }
+    __device__ int64_t row0(int b) const { return r[b]; }
+    __device__ uint32_t cost0(int b) const { return c[b]; }
+    __device__ int64_t key0(int b) const { return k[b]; }
 };
-__device__ __forceinline__ TilePos split_tile(const Split& sp, uint32_t p) {
-    TilePos tp;
-    tp.unit = (int)(p / sp.W);
-    const uint32_t r = p - (uint32_t)tp.unit * sp.W;
-    tp.tile = r <= kSegCost4 ? 0 : (int)((r - kSegCost4 + 3) / 4);
-    if (tp.tile >= sp.nt) {
-        ++tp.unit;
-        tp.tile = 0;
-    }
-    return tp;
-}
-// Workgroup (in list order) whose stretch holds cost step p.
-__host__ __device__ inline int stretch_of(const Split& sp, uint32_t p) {
-    int v = (int)((double)p * (double)sp.nwg / (double)sp.Wt);
-    if (v > sp.nwg - 1) v = sp.nwg - 1;
-    while (v + 1 < sp.nwg && stretch_start(sp, v + 1) <= p) ++v;
-    while (v > 0 && stretch_start(sp, v) > p) --v;
-    return v;
-}
-
-// Position in a workgroup's stretch: keys walked since the stretch start (a
-// stretch is far below 2^31 keys), unit and key inside the unit.  Advanced tile by
-// tile without division; all bookkeeping is 32-bit scalar work.
-struct Walker {
-    int x;
-    int unit, key0;
-};
-struct Tile {
-    int unit, key0, nkeys;
-    bool seg_start, seg_end;
-};
-// `len` = keys in the stretch.
-__device__ __forceinline__ Tile peek(const Walker& w, int len, int S) {
-    Tile t;
-    t.unit = w.unit;
-    t.key0 = w.key0;
-    int n = kTileKeys;
-    if (S - w.key0 < n) n = S - w.key0;
-    if (len - w.x < n) n = len - w.x;
-    t.nkeys = n;
-    t.seg_start = (w.x == 0) || (w.key0 == 0);
-    t.seg_end = (w.x + n == len) || (w.key0 + n == S);
-    return t;
-}
-__device__ __forceinline__ void advance(Walker& w, int nkeys, int S) {
-    w.x += nkeys;
-    w.key0 += nkeys;
-    if (w.key0 == S) {
-        w.key0 = 0;
-        ++w.unit;
-    }
-}
 
 // Packed query row -> (tree row, query head); rows past G*T map to row 0.
 __device__ __forceinline__ void query_row(const AttnArgs& a, int g, int rp, int& i, int& hq) {
@@ -303,6 +248,10 @@ __device__ __forceinline__ void query_row(const AttnArgs& a, int g, int rp, int&
     const int gi = rp / a.T;
     i = rp - gi * a.T;
     hq = g * a.G + gi;
+}
+// Element offset of (sequence b, tree row i, query head hq) in q / o.
+__device__ __forceinline__ int64_t qo_row(const AttnArgs& a, int b, int i, int hq) {
+    return (((int64_t)b * a.T + i) * a.Hq + hq) * kD;
 }
 
 // Direct-to-LDS loads of one tile's K and V rows, all issued by the loader wave:
@@ -314,8 +263,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const Tile& t, int6
                                           const uint32_t (&off4)[4], int li, int lane) {
     // keep the wave's outstanding-load count within the 63 its counter holds
     vm_wait<63 - kTileLoads>();
-    const int g = t.unit / a.RG;
-    const int64_t elt0 = ((int64_t)g * a.kv_rows_total + row0 + t.key0) * kD;
+    const int64_t elt0 = ((int64_t)t.g * a.kv_rows_total + row0 + t.key0) * kD;
     const __bf16* kb = a.k + elt0;
     const __bf16* vb = a.v + elt0;
     if (t.nkeys == kTileKeys) {
@@ -350,23 +298,23 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const Tile& t, int6
 
 // Direct-to-LDS loads of a unit's 64 packed Q rows and their mask words, by the
 // loader wave: 16 + 2 loads per lane.
-__device__ __forceinline__ void load_q(const AttnArgs& a, int unit, unsigned char* qslot, uint32_t* mslot,
+__device__ __forceinline__ void load_q(const AttnArgs& a, const Tile& t, unsigned char* qslot, uint32_t* mslot,
                                        int li, int lane) {
     vm_wait<63 - kQLoads>();  // at most 63 loads in flight
-    const int g = unit / a.RG, rg = unit - g * a.RG;
+    const __bf16* qb = a.q + qo_row(a, t.b, 0, 0);
 #pragma unroll
     for (int bi = 0; bi < 16 / kLoaders; ++bi) {
         const int blk = bi * kLoaders + li;
         const int rho = blk * 4 + (lane >> 4);
         int i, hq;
-        query_row(a, g, rg * kUnitRows + rho, i, hq);
+        query_row(a, t.g, t.rg * kUnitRows + rho, i, hq);
         const uint32_t off = (uint32_t)((((int64_t)i * a.Hq + hq) * kD) * 2 + (((lane & 15) ^ swz(rho)) << 4));
-        dma_b128(a.q, off, lds_u32(qslot + blk * 1024));
+        dma_b128(qb, off, lds_u32(qslot + blk * 1024));
     }
     if (li == 0) {
         int i, hq;
-        query_row(a, g, rg * kUnitRows + lane, i, hq);
-        const uint32_t* mw = (const uint32_t*)(a.mask + i);
+        query_row(a, t.g, t.rg * kUnitRows + lane, i, hq);
+        const uint32_t* mw = (const uint32_t*)(a.mask + (int64_t)t.b * a.T + i);
         dma_b32(mw, lds_u32(mslot));
         dma_b32(mw + 1, lds_u32(mslot + kWave));
     }
@@ -375,11 +323,10 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int unit, unsigned cha
 // The tile walk of one workgroup, for the loader wave (kLoader) or a computing
 // wave.  Both instantiations share every branch that reaches a barrier, so the
 // five waves always meet the same barriers in the same order.
-template <bool kLoader>
-__device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem, unsigned char* qslot,
-                                          uint32_t* mslot, float (*s_ml)[2][2][kWave], int wid, int lane,
-                                          int T, int ctx, int S, int64_t row0, int vwg, int len,
-                                          TilePos tb) {
+template <bool kLoader, class Tab>
+__device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, unsigned char* smem,
+                                          unsigned char* qslot, uint32_t* mslot, float (*s_ml)[2][2][kWave],
+                                          int wid, int lane, int vwg, int len, Pos tb) {
     constexpr bool loader = kLoader;
     const int rb = wid & 1, ks = (wid >> 1) & 1;
     const int l32 = lane & 31, h2 = lane >> 5;
@@ -391,23 +338,21 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     for (int j = 0; j < 4; ++j)
         off4[j] = (uint32_t)((lane >> 4) * kRowBytes + (((lane & 15) ^ swz(j * 4 + (lane >> 4))) << 4));
 
-    Walker w0;
-    w0.x = 0;
-    w0.unit = tb.unit;
-    w0.key0 = tb.tile * kTileKeys;
+    const int T = a.T;
+    const int B = a.B, UPS = a.Hkv * a.RG;
+    Walker w0 = plan::walker_at(tab, a.RG, tb);
 
     // ---- first segment's Q and mask word, straight into registers ----
     const int qrow = 32 * rb + l32;  // this lane's packed query row inside the unit
     bf16x8 qcur[8];
     uint64_t mword_n;
-    auto load_q_direct = [&](int unit) {
-        const int g = unit / a.RG, rg = unit - g * a.RG;
+    auto load_q_direct = [&](const Tile& t) {
         int i, hq;
-        query_row(a, g, rg * kUnitRows + qrow, i, hq);
-        const __bf16* qp = a.q + ((int64_t)i * a.Hq + hq) * kD;
+        query_row(a, t.g, t.rg * kUnitRows + qrow, i, hq);
+        const __bf16* qp = a.q + qo_row(a, t.b, i, hq);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qcur[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * h2);
-        mword_n = a.mask[i];
+        mword_n = a.mask[(int64_t)t.b * T + i];
         wait_direct_loads();
     };
 
@@ -432,15 +377,16 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
     // keeps the slot free from the start for the next segment's Q, which rides with
     // that segment's first tile (a third segment starting while the slot is still
     // busy loads its Q directly when its scores are computed).
-    if (!loader) load_q_direct(w0.unit);
+    if (!loader) load_q_direct(plan::peek(w0, len));
     auto fetch = [&]() {
-        const Tile t = peek(wf, len, S);
-        if (loader) load_tile(a, t, row0, smem + (nl % kStages) * kStageBytes, off4, wid - kComputeWaves, lane);
+        const Tile t = plan::peek(wf, len);
+        if (loader)
+            load_tile(a, t, t.row0, smem + (nl % kStages) * kStageBytes, off4, wid - kComputeWaves, lane);
         if (t.seg_start && nl > 0 && q_slot_tile < 0) {
-            if (loader) load_q(a, t.unit, qslot, mslot, wid - kComputeWaves, lane);
+            if (loader) load_q(a, t, qslot, mslot, wid - kComputeWaves, lane);
             q_slot_tile = nl;
         }
-        advance(wf, t.nkeys, S);
+        plan::advance(wf, t.nkeys, tab, B, a.RG, UPS);
         ++nl;
     };
     fetch();
@@ -474,8 +420,8 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
 
     // ---- tile 0: scores ----
     Walker wn = w0;           // tile whose scores are computed next
-    Tile tc = peek(wn, len, S);
-    advance(wn, tc.nkeys, S);
+    Tile tc = plan::peek(wn, len);
+    plan::advance(wn, tc.nkeys, tab, B, a.RG, UPS);
     f32x16 sacc;
     if (!loader) sacc = scores(smem);
     uint64_t mword_c = mword_n;
@@ -499,7 +445,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
             if (loader) loader_wait(nl - it - 2);
             barrier_lds();
             if (wf.x < len) fetch();
-            tn = peek(wn, len, S);
+            tn = plan::peek(wn, len);
             if (tn.seg_start) {
                 if (q_slot_tile == it + 1) {
                     if (!loader) {
@@ -507,7 +453,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
                     }
                     q_slot_tile = -1;  // free once every wave has passed the next barrier
                 } else if (!loader) {
-                    load_q_direct(tn.unit);  // rare (short segments)
+                    load_q_direct(tn);  // rare (short segments)
                 }
                 from0_n = tn.key0 == 0;
             }
@@ -519,6 +465,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
 
         // ---- online softmax (base 2): lane = one query row, 16 of its keys ----
         // Raw scores; the scale (> 0) is applied inside the exponent.
+        const int ctx = tc.S - T;
         if (tc.key0 + kTileKeys > ctx || tc.nkeys < kTileKeys) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -636,8 +583,9 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
                 s_ml[ks][rb][1][lane] = lw;
             }
             barrier_lds();
-            const int g = tc.unit / a.RG, rg = tc.unit - g * a.RG;
-            const bool whole = from0_c && tc.key0 + tc.nkeys == S;
+            const int g = tc.g, rg = tc.rg;
+            const bool whole = from0_c && tc.key0 + tc.nkeys == tc.S;
+            const int slot = plan::part_slot(vwg, from0_c);
             if (!loader) {
                 const float m1 = s_ml[ks ^ 1][rb][0][lane], l1 = s_ml[ks ^ 1][rb][1][lane];
                 const float M = fmaxf(m_run, m1);
@@ -694,12 +642,11 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
                         if (a.lse) {
                             int i, hq;
                             query_row(a, g, rp, i, hq);
-                            a.lse[(int64_t)i * a.Hq + hq] = (M + log2f(ltot)) * kLn2;
+                            a.lse[((int64_t)tc.b * T + i) * a.Hq + hq] = (M + log2f(ltot)) * kLn2;
                         }
                     } else {
-                        const int64_t slot = (int64_t)tc.unit + vwg;
-                        a.part_ml[slot * 128 + qrow] = M;
-                        a.part_ml[slot * 128 + 64 + qrow] = ltot;
+                        a.part_ml[(int64_t)slot * kUnitRows + qrow] =
+                            ((uint64_t)__float_as_uint(ltot) << 32) | __float_as_uint(M);
                     }
                 }
             }
@@ -720,11 +667,11 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
                         if (rp < a.G * T) {
                             int i, hq;
                             query_row(a, g, rp, i, hq);
-                            *reinterpret_cast<u32x4*>(a.o + ((int64_t)i * a.Hq + hq) * kD + 8 * (ln & 15)) = val[r4];
+                            *reinterpret_cast<u32x4*>(a.o + qo_row(a, tc.b, i, hq) + 8 * (ln & 15)) = val[r4];
                         }
                     }
                 } else {
-                    _Float16* const po = a.part_o + ((int64_t)tc.unit + vwg) * (kUnitRows * kD);
+                    _Float16* const po = a.part_o + (int64_t)slot * (kUnitRows * kD);
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int row = 16 * wid + 4 * r4 + (ln >> 4);
@@ -744,14 +691,56 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, unsigned char* smem
         if (!has_next) break;
         sacc = snext;
         tc = tn;
-        advance(wn, tn.nkeys, S);
+        plan::advance(wn, tn.nkeys, tab, B, a.RG, UPS);
         mword_c = mword_n;
         from0_c = from0_n;
     }
 }
 
-// kHostLen: the sequence's context length and first row come as launch arguments
-// (a separate instantiation, so every argument load issues at once).
+// The per-sequence table of a launch built in LDS by wave 0 from the sequences'
+// lengths and first rows: S = ctx + T, cost and key prefixes (wave scans).
+__device__ __forceinline__ void build_table(const int32_t* ctx_len, const int64_t* kv_row_off, int B, int T,
+                                            int UPS, int32_t* s_S, int64_t* s_row0, uint32_t* s_cost0,
+                                            int64_t* s_key0, int lane) {
+    uint32_t cost_run = 0;
+    int64_t key_run = 0;
+    for (int base = 0; base < B; base += kWave) {
+        const int b = base + lane;
+        int S = 0;
+        if (b < B) {
+            S = ctx_len[b] + T;
+            s_S[b] = S;
+            s_row0[b] = kv_row_off[b];
+        }
+        uint32_t ci = b < B ? (uint32_t)UPS * plan::unit_cost(S) : 0u;
+        int64_t ki = b < B ? (int64_t)UPS * S : 0;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t cu = __shfl_up(ci, off, kWave);
+            const uint32_t klo = __shfl_up((uint32_t)ki, off, kWave);
+            const uint32_t khi = __shfl_up((uint32_t)((uint64_t)ki >> 32), off, kWave);
+            if (lane >= off) {
+                ci += cu;
+                ki += (int64_t)(((uint64_t)khi << 32) | klo);
+            }
+        }
+        if (b < B) {
+            s_cost0[b + 1] = cost_run + ci;
+            s_key0[b + 1] = key_run + ki;
+        }
+        cost_run += __shfl(ci, kWave - 1, kWave);
+        key_run += (int64_t)(((uint64_t)__shfl((uint32_t)((uint64_t)ki >> 32), kWave - 1, kWave) << 32) |
+                             __shfl((uint32_t)ki, kWave - 1, kWave));
+    }
+    if (lane == 0) {
+        s_cost0[0] = 0;
+        s_key0[0] = 0;
+    }
+}
+
+// One launch covers B <= plan::kMaxSeqs sequences.  kHostLen: the host computed
+// the launch plan (B <= kArgSeqs), read from the launch arguments; otherwise the
+// kernel reads the lengths and builds the plan itself.
 template <bool kHostLen>
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
@@ -761,106 +750,132 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int T = a.T;
-    const int ctx = kHostLen ? a.ctx_h : a.ctx_len[0];
-    const int S = ctx + T;
-    const int64_t row0 = kHostLen ? a.row0_h : a.kv_row_off[0];
-    const int units = a.Hkv * a.RG;
-    const Split sp = make_split(S, units, (int)gridDim.x);
+    const int B = a.B;
+    const int UPS = a.Hkv * a.RG;
     const int xcd = blockIdx.x & 7;
-    const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
-    if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
-    const TilePos tb = split_tile(sp, stretch_start(sp, vwg));
-    const TilePos te = split_tile(sp, stretch_start(sp, vwg + 1));
-    const int64_t x_begin = (int64_t)tb.unit * S + tb.tile * kTileKeys;
-    const int64_t x_end = (int64_t)te.unit * S + te.tile * kTileKeys;
-    if (x_begin >= x_end) return;  // a stretch in the steps before a unit's first tile
-    const int len = (int)(x_end - x_begin);
-
-    // waves 0..3 compute (query half, key half); wave 4 issues every K, V and Q
-    // load and waits for them, so no computing wave stalls on a load issue.  Both
+    // waves 0..3 compute (query half, key half); waves 4..7 issue every K, V and Q
+    // load and wait for them, so no computing wave stalls on a load issue.  Both
     // roles run the same tile walk and the same barriers.
-    if (wid >= kComputeWaves)
-        tile_loop<true>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, len, tb);
-    else
-        tile_loop<false>(a, smem, qslot, mslot, s_ml, wid, lane, T, ctx, S, row0, vwg, len, tb);
-
+    auto walk = [&](const auto& tab, int vwg, int len, const Pos& tb) {
+        if (wid >= kComputeWaves)
+            tile_loop<true>(a, tab, smem, qslot, mslot, s_ml, wid, lane, vwg, len, tb);
+        else
+            tile_loop<false>(a, tab, smem, qslot, mslot, s_ml, wid, lane, vwg, len, tb);
+    };
+    if constexpr (kHostLen) {
+        const ArgTab tab{&a.hp};
+        const Split sp = plan::make_split(a.hp.cost0[B], (int)gridDim.x, B * UPS);
+        const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
+        if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
+        const Pos tb = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, vwg));
+        const Pos te = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, vwg + 1));
+        const int64_t x_begin = plan::key_index(tab, B, tb), x_end = plan::key_index(tab, B, te);
+        if (x_begin >= x_end) return;  // a stretch in the steps before a unit's first tile
+        walk(tab, vwg, (int)(x_end - x_begin), tb);
+    } else {
+        __shared__ int32_t s_S[plan::kMaxSeqs];
+        __shared__ int64_t s_row0[plan::kMaxSeqs];
+        __shared__ uint32_t s_cost0[plan::kMaxSeqs + 1];
+        __shared__ int64_t s_key0[plan::kMaxSeqs + 1];
+        if (wid == 0) build_table(a.ctx_len, a.kv_row_off, B, a.T, UPS, s_S, s_row0, s_cost0, s_key0, lane);
+        __syncthreads();
+        const LdsTab tab{s_S, s_row0, s_cost0, s_key0};
+        const Split sp = plan::make_split(s_cost0[B], (int)gridDim.x, B * UPS);
+        const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
+        if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;
+        const Pos tb = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, vwg));
+        const Pos te = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, vwg + 1));
+        const int64_t x_begin = plan::key_index(tab, B, tb), x_end = plan::key_index(tab, B, te);
+        if (x_begin >= x_end) return;
+        walk(tab, vwg, (int)(x_end - x_begin), tb);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one workgroup per (unit, 16 query rows); thread = (row, 8 dims).
-// Partials are combined kMergeBatch at a time, their loads issued together.
-// Workgroup b: XCD x = b % 8, then the (b / 8)-th (unit, row block) of the units
-// XCD x merges; the grid holds 8 * ceil(units / 8) * kRowBlocks workgroups.
+// Merge: one workgroup per (split unit, 16 query rows); thread = (row, 8 dims).
+// The partials of the unit's pieces are combined kMergeBatch at a time, their
+// loads issued together.  With a host plan, workgroup blk runs on XCD blk % 8
+// and merges rows of a unit whose middle piece that XCD computed (most of its
+// partials are still in that XCD's L2); without one, workgroup (v, row block)
+// merges the split unit whose first stretch is v, if any.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
 constexpr int kRowBlocks = kUnitRows / 16;
-
-// Per merge workgroup, its unit and that unit's first and last stretch (where its
-// partials are), computed on the host when the context length is known there: the
-// word is read by workgroup index alone, together with the other launch arguments,
-// so the kernel starts its loads without the split arithmetic (about 0.9 us at its
-// start).  Entry: bit 31 set = unit in use, bits 16..23 unit, 8..15 first stretch,
-// 0..7 last stretch.  Up to kPlanWgs merge workgroups (64 units).
-constexpr int kPlanWgs = 256;
+constexpr int kPlanWgs = 384;  // merge workgroups a host plan covers (96 split units)
+// Per merge workgroup: bit 63 set = in use, then b (bits 0..15), uis (16..39), vf
+// (40..47), vl (48..55), row block (56..57); read by workgroup index alone.
 struct MergePlan {
-    int n_wg;                       // workgroups covered (0: computed in the kernel)
-    uint32_t e[kPlanWgs];
+    uint64_t e[kPlanWgs];
 };
-static_assert(kGridWG <= 256, "stretch indices fit 8 bits");
+struct MergeArgs {
+    __bf16* o;
+    float* lse;
+    const _Float16* part_o;
+    const uint64_t* part_ml;
+    const int32_t* ctx_len;
+    const int64_t* kv_row_off;
+    int B, T, Hq, Hkv, G, RG;
+    MergePlan mp;  // kHostPlan only
+};
 
-template <bool kHostLen>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int grid_wg, MergePlan plan) {
+template <bool kHostPlan>
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
     const int tid = threadIdx.x;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    int unit, vf, vl;
-    if (kHostLen && plan.n_wg > 0) {
-        const uint32_t e = plan.e[blockIdx.x];
-        if (!(e >> 31)) return;
-        unit = (int)((e >> 16) & 0xFFu);
-        vf = (int)((e >> 8) & 0xFFu);
-        vl = (int)(e & 0xFFu);
+    int b, uis, vf, vl, rb;
+    if constexpr (kHostPlan) {
+        const uint64_t e = m.mp.e[blockIdx.x];
+        if (!(e >> 63)) return;
+        b = (int)(e & 0xFFFFu);
+        uis = (int)((e >> 16) & 0xFFFFFFu);
+        vf = (int)((e >> 40) & 0xFFu);
+        vl = (int)((e >> 48) & 0xFFu);
+        rb = (int)((e >> 56) & 3u);
     } else {
-        const int units = a.Hkv * a.RG;
-        unit = merge_unit_first(xcd, units) + j / kRowBlocks;
-        if (unit >= merge_unit_first(xcd + 1, units)) return;
-        const int S = (kHostLen ? a.ctx_h : a.ctx_len[0]) + a.T;
-        const Split sp = make_split(S, units, grid_wg);
-        const uint32_t p0 = (uint32_t)unit * sp.W + kSegCost4;  // cost step of the unit's first tile
-        vf = stretch_of(sp, p0);
-        vl = stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
+        __shared__ int32_t s_S[plan::kMaxSeqs];
+        __shared__ int64_t s_row0[plan::kMaxSeqs];
+        __shared__ uint32_t s_cost0[plan::kMaxSeqs + 1];
+        __shared__ int64_t s_key0[plan::kMaxSeqs + 1];
+        const int UPS = m.Hkv * m.RG;
+        if (tid < kWave) build_table(m.ctx_len, m.kv_row_off, m.B, m.T, UPS, s_S, s_row0, s_cost0, s_key0, tid);
+        __syncthreads();
+        const LdsTab tab{s_S, s_row0, s_cost0, s_key0};
+        const Split sp = plan::make_split(s_cost0[m.B], kGridWG, m.B * UPS);
+        const int v = blockIdx.x / kRowBlocks;
+        rb = blockIdx.x % kRowBlocks;
+        if (v >= sp.nwg) return;
+        const Pos te = plan::split_tile(tab, m.B, UPS, plan::stretch_start(sp, v + 1));
+        if (!plan::split_unit_from(tab, sp, m.B, UPS, v, te, b, uis, vl)) return;
+        vf = v;
     }
-    if (vf == vl) return;  // written directly by the main kernel
-    const int g = unit / a.RG, rg = unit - g * a.RG;
-    const int row = (j % kRowBlocks) * 16 + (tid >> 4);
+    const int g = uis / m.RG, rg = uis - g * m.RG;
+    const int row = rb * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
     const int rp = rg * kUnitRows + row;
-    if (rp >= a.G * a.T) return;
+    if (rp >= m.G * m.T) return;
     float M = -INFINITY, L = 0.0f;
     float acc[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) acc[x] = 0.0f;
-    // up to kMergeBatch partials per round, all requested together: slots past the
-    // last re-read the last one (same addresses) and get zero weight
     for (int v0 = vf; v0 <= vl; v0 += kMergeBatch) {
-        float mv[kMergeBatch], lv[kMergeBatch];
+        uint64_t ml[kMergeBatch];
         f16x8 ov[kMergeBatch];
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-            const int64_t slot = (int64_t)unit + (v0 + j <= vl ? v0 + j : vl);
-            mv[j] = a.part_ml[slot * 128 + row];
-            lv[j] = a.part_ml[slot * 128 + 64 + row];
-            ov[j] = *(const f16x8*)(a.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
+            // pieces past the last re-read the last one and get zero weight
+            const int v = v0 + j <= vl ? v0 + j : vl;
+            const int64_t slot = plan::part_slot(v, v == vf);
+            ml[j] = m.part_ml[slot * kUnitRows + row];
+            ov[j] = *(const f16x8*)(m.part_o + slot * (kUnitRows * kD) + (int64_t)row * kD + d0);
         }
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j)
-            if (v0 + j > vl) {
-                mv[j] = -INFINITY;
-                lv[j] = 0.0f;
-            }
+        float mv[kMergeBatch], lv[kMergeBatch];
         float Mn = M;
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, mv[j]);
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const bool live = v0 + j <= vl;
+            mv[j] = live ? __uint_as_float((uint32_t)ml[j]) : -INFINITY;
+            lv[j] = live ? __uint_as_float((uint32_t)(ml[j] >> 32)) : 0.0f;
+            Mn = fmaxf(Mn, mv[j]);
+        }
         const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
         const float sc = __builtin_amdgcn_exp2f(M - Mu);
         L *= sc;
@@ -868,6 +883,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
         for (int x = 0; x < 8; ++x) acc[x] *= sc;
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
+            // a piece that saw none of a row's keys has (max -inf, sum 0): weight 0
             const float w = __builtin_amdgcn_exp2f(mv[j] - Mu) * lv[j];
             L += w;
 #pragma unroll
@@ -875,14 +891,13 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a, int gr
         }
         M = Mn;
     }
-    int i, hq;
-    query_row(a, g, rp, i, hq);
+    const int gi = rp / m.T, i = rp - gi * m.T, hq = g * m.G + gi;
     const float inv = 1.0f / L;
     bf16x8 out;
 #pragma unroll
     for (int x = 0; x < 8; ++x) out[x] = (__bf16)(acc[x] * inv);
-    *(bf16x8*)(a.o + ((int64_t)i * a.Hq + hq) * kD + d0) = out;
-    if (d0 == 0 && a.lse) a.lse[(int64_t)i * a.Hq + hq] = (M + log2f(L)) * kLn2;
+    *(bf16x8*)(m.o + (((int64_t)b * m.T + i) * m.Hq + hq) * kD + d0) = out;
+    if (d0 == 0 && m.lse) m.lse[((int64_t)b * m.T + i) * m.Hq + hq] = (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1015,17 +1030,54 @@ struct WsLayout {
     size_t part_o, part_ml, total;
 };
 
-// Partial slots for one sequence (reused, in stream order, by the next one).
+// Partial slots of one launch (reused, in stream order, by the next launch).
 WsLayout ws_layout(const eagle_attn_desc& d) {
     WsLayout w{0, 0, 0};
     if (d.dtype != EAGLE_BF16) return w;
-    const int G = d.n_q_heads / d.n_kv_heads;
-    const int RG = (G * d.T + kUnitRows - 1) / kUnitRows;
-    const size_t slots = (size_t)d.n_kv_heads * RG + kGridWG;
+    const size_t slots = 2 * (size_t)kGridWG;
     w.part_o = 0;
     w.part_ml = align_up(slots * kUnitRows * kD * sizeof(_Float16));
-    w.total = w.part_ml + align_up(slots * 2 * kUnitRows * sizeof(float));
+    w.total = w.part_ml + align_up(slots * kUnitRows * sizeof(uint64_t));
     return w;
+}
+
+// The per-sequence table of up to kArgSeqs sequences, and the merge plan: the
+// split units (found as the merge kernel would find them), each of its row blocks
+// on the XCD that computed the unit's middle piece.  Returns the merge workgroups
+// to launch, or -1 when the plan does not fit kPlanWgs (the merge kernel then
+// finds the split units itself).
+int host_plan(HostPlan& hp, MergePlan& mp, const int32_t* ctx, const int64_t* row0, int B, int T, int UPS) {
+    hp.cost0[0] = 0;
+    hp.key0[0] = 0;
+    for (int b = 0; b < B; ++b) {
+        hp.S[b] = ctx[b] + T;
+        hp.row0[b] = row0[b];
+        hp.cost0[b + 1] = hp.cost0[b] + (uint32_t)UPS * plan::unit_cost(hp.S[b]);
+        hp.key0[b + 1] = hp.key0[b] + (int64_t)UPS * hp.S[b];
+    }
+    const ArgTab tab{&hp};
+    const Split sp = plan::make_split(hp.cost0[B], kGridWG, B * UPS);
+    uint64_t by_xcd[8][kPlanWgs];
+    int n_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int v = 0; v < sp.nwg; ++v) {
+        int b, uis, vl;
+        const Pos te = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, v + 1));
+        if (!plan::split_unit_from(tab, sp, B, UPS, v, te, b, uis, vl)) continue;
+        const int mid = (v + vl) / 2;
+        int x = 0;
+        while (x < 7 && xcd_first(x + 1, sp.nwg) <= mid) ++x;
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+            if (n_xcd[x] == kPlanWgs / 8) return -1;
+            by_xcd[x][n_xcd[x]++] = (1ull << 63) | (uint64_t)(uint32_t)b | ((uint64_t)(uint32_t)uis << 16) |
+                                    ((uint64_t)v << 40) | ((uint64_t)vl << 48) | ((uint64_t)rb << 56);
+        }
+    }
+    int most = 0;
+    for (int x = 0; x < 8; ++x) most = n_xcd[x] > most ? n_xcd[x] : most;
+    // workgroup blk = 8 j + x runs on XCD x and takes that XCD's j-th entry
+    for (int j = 0; j < most; ++j)
+        for (int x = 0; x < 8; ++x) mp.e[8 * j + x] = j < n_xcd[x] ? by_xcd[x][j] : 0;
+    return 8 * most;
 }
 
 }  // namespace
@@ -1034,10 +1086,13 @@ size_t attention_workspace_bytes(const eagle_attn_desc& d) { return ws_layout(d)
 
 bool attention_split_fits(const eagle_attn_desc& d) {
     if (d.dtype != EAGLE_BF16) return true;
+    // the cost line of one launch, bounded through sum_b ceil(S_b / 64) <=
+    // ceil(kv_rows_total / 64) + B (the sequences' rows lie inside the cache)
     const int64_t G = d.n_q_heads / d.n_kv_heads;
-    const int64_t units = (int64_t)d.n_kv_heads * ((G * d.T + kUnitRows - 1) / kUnitRows);
-    const int64_t tiles = (d.kv_rows_total + kTileKeys - 1) / kTileKeys;  // bounds ctx + T of any sequence
-    return units * (4 * tiles + kSegCost4) < ((int64_t)1 << 31);
+    const int64_t ups = (int64_t)d.n_kv_heads * ((G * d.T + kUnitRows - 1) / kUnitRows);
+    const int64_t B = d.batch < plan::kMaxSeqs ? d.batch : plan::kMaxSeqs;
+    const int64_t tiles = (d.kv_rows_total + kTileKeys - 1) / kTileKeys + B;
+    return ups * (4 * tiles + (int64_t)plan::kSegCost * B) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k, const void* v,
@@ -1056,60 +1111,53 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
     }
     const WsLayout w = ws_layout(d);
     unsigned char* ws = (unsigned char*)workspace;
-    const int RG = (G * d.T + kUnitRows - 1) / kUnitRows;
     const size_t seq_q = (size_t)d.T * d.n_q_heads * kD;
-    // One sequence per launch pair: the kernels never walk across sequences.
-    for (int b = 0; b < d.batch; ++b) {
+    const int RG = (G * d.T + kUnitRows - 1) / kUnitRows;
+    const int UPS = d.n_kv_heads * RG;
+    // One main launch per plan::kMaxSeqs sequences: the split covers every
+    // sequence of the launch, so workgroups walk from one sequence's units into
+    // the next; then one merge launch for the units split between workgroups.
+    for (int b0 = 0; b0 < d.batch; b0 += plan::kMaxSeqs) {
+        const int nb = d.batch - b0 < plan::kMaxSeqs ? d.batch - b0 : plan::kMaxSeqs;
         AttnArgs a;
-        a.q = (const __bf16*)q + b * seq_q;
+        a.q = (const __bf16*)q + b0 * seq_q;
         a.k = (const __bf16*)k;
         a.v = (const __bf16*)v;
-        a.mask = mask + (size_t)b * d.T;
-        a.o = (__bf16*)o + b * seq_q;
-        a.lse = lse ? lse + (size_t)b * d.T * d.n_q_heads : nullptr;
-        a.ctx_len = d.ctx_len + b;
-        a.kv_row_off = d.kv_row_off + b;
+        a.mask = mask + (size_t)b0 * d.T;
+        a.o = (__bf16*)o + b0 * seq_q;
+        a.lse = lse ? lse + (size_t)b0 * d.T * d.n_q_heads : nullptr;
+        a.ctx_len = d.ctx_len + b0;
+        a.kv_row_off = d.kv_row_off + b0;
         a.part_o = (_Float16*)(ws + w.part_o);
-        a.part_ml = (float*)(ws + w.part_ml);
+        a.part_ml = (uint64_t*)(ws + w.part_ml);
         a.kv_rows_total = d.kv_rows_total;
-        a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
+        a.B = nb; a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
         a.scale_log2 = scale * kLog2e;
-        a.ctx_h = d.ctx_len_host ? d.ctx_len_host[b] : -1;
-        a.row0_h = d.kv_row_off_host ? d.kv_row_off_host[b] : 0;
-        if (a.ctx_h >= 0)  // 4 computing waves + 4 loaders per workgroup
-            tree_attn_bf16_kernel<true><<<kGridWG, kThreads, 0, stream>>>(a);
-        else
+        MergeArgs m;
+        m.o = a.o;
+        m.lse = a.lse;
+        m.part_o = a.part_o;
+        m.part_ml = a.part_ml;
+        m.ctx_len = a.ctx_len;
+        m.kv_row_off = a.kv_row_off;
+        m.B = nb; m.T = d.T; m.Hq = d.n_q_heads; m.Hkv = d.n_kv_heads; m.G = G; m.RG = RG;
+        // the merge plan packs (sequence, unit) in 16 + 24 bits
+        const bool host = d.ctx_len_host && nb <= kArgSeqs && UPS < (1 << 24);
+        hipError_t e;
+        if (host) {
+            const int merge_wg = host_plan(a.hp, m.mp, d.ctx_len_host + b0, d.kv_row_off_host + b0, nb, d.T, UPS);
+            tree_attn_bf16_kernel<true><<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + 4 loaders
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (merge_wg > 0)
+                tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(m);
+            else if (merge_wg < 0)
+                tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
+        } else {
             tree_attn_bf16_kernel<false><<<kGridWG, kThreads, 0, stream>>>(a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int units = d.n_kv_heads * RG;
-        const int merge_wg = 8 * ((units + 7) / 8) * kRowBlocks;
-        MergePlan plan;
-        plan.n_wg = 0;
-        if (a.ctx_h >= 0 && merge_wg <= kPlanWgs) {
-            // the same split the main kernel makes, and the same workgroup -> unit map
-            // the merge kernel would compute, evaluated here once
-            const Split sp = make_split(a.ctx_h + d.T, units, kGridWG);
-            for (int wg = 0; wg < merge_wg; ++wg) {
-                const int xcd = wg & 7, j = wg >> 3;
-                const int u = merge_unit_first(xcd, units) + j / kRowBlocks;
-                uint32_t e = 0;
-                if (u < merge_unit_first(xcd + 1, units)) {
-                    const uint32_t p0 = (uint32_t)u * sp.W + kSegCost4;
-                    const uint32_t vf = (uint32_t)stretch_of(sp, p0);
-                    const uint32_t vl = (uint32_t)stretch_of(sp, p0 + 4u * (uint32_t)(sp.nt - 1));
-                    e = (1u << 31) | ((uint32_t)u << 16) | (vf << 8) | vl;
-                }
-                plan.e[wg] = e;
-            }
-            plan.n_wg = merge_wg;
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
         }
-        if (a.ctx_h >= 0)
-            tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(a, kGridWG, plan);
-        else
-            tree_attn_merge_kernel<false><<<merge_wg, 256, 0, stream>>>(a, kGridWG, plan);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }

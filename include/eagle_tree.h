@@ -159,13 +159,15 @@ int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
  * kv_rows_total must be at least sum_b (ctx_len[b] + T) (not checkable on the
  * host; the call checks kv_rows_total >= batch * T).
  * Supported: BF16 with head_dim 128; F32 with head_dim <= 128; T <= 64;
- * batch <= EAGLE_MAX_BATCH; for BF16 also
- *     n_kv_heads * ceil(G * T / 64) * (4 * ceil(kv_rows_total / 64) + 16) < 2^31,
+ * batch <= EAGLE_MAX_BATCH; for BF16 also, with B = min(batch, 256),
+ *     n_kv_heads * ceil(G * T / 64) * (4 * (ceil(kv_rows_total / 64) + B) + 16 * B) < 2^31,
  * G = n_q_heads / n_kv_heads (otherwise EAGLE_ERR_UNSUPPORTED).  BF16 runs one
- * sequence per kernel launch pair.
- * The workspace (eagle_tree_attention_workspace bytes, none for F32) holds
- * split-KV partials; it needs no initialisation, and calls that share one must
- * be ordered on one stream.
+ * main kernel launch per 256 sequences -- the (sequence, KV head, row group)
+ * units of all of them are split over the GPU's compute units together -- and one
+ * merge launch for the units split between workgroups (none when no unit is).
+ * The workspace (eagle_tree_attention_workspace bytes, the same for every BF16
+ * shape; none for F32) holds the split-KV partials; it needs no initialisation,
+ * and calls that share one must be ordered on one stream.
  * ctx_len_host / kv_row_off_host: optional host copies of ctx_len and kv_row_off
  * (both or neither; NULL = the kernels read the device arrays).  When given they
  * must hold the same values as the device arrays, and the BF16 kernels take each
@@ -196,12 +198,14 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same operation, arguments, layouts, kernels and results
  * (bit for bit) as eagle_tree_attention; the split-KV partials live in a
- * file-scope device array of EAGLE_NOALLOC_SCRATCH_BYTES that the library holds
- * on each GPU it runs on until the process ends (its address is taken once per
- * device, on the first call with that device current; `stream` must belong to
- * the current device).  The call allocates and frees nothing.  A shape whose
- * eagle_tree_attention_workspace exceeds EAGLE_NOALLOC_SCRATCH_BYTES is
- * EAGLE_ERR_WORKSPACE (nothing launched); other checks as eagle_tree_attention.
+ * file-scope device array of EAGLE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its address is taken once per
+ * device, on the first call with that device current; `stream` must belong to the
+ * current device).  Nothing in it needs clearing between calls.  The call
+ * allocates and frees nothing.  A shape whose eagle_tree_attention_workspace
+ * exceeded EAGLE_NOALLOC_SCRATCH_BYTES would get EAGLE_ERR_WORKSPACE (nothing
+ * launched; the BF16 workspace is about 4.5 MB for every shape, so none does);
+ * other checks as eagle_tree_attention.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (other streams, other threads) race; order them on one stream. */
 #define EAGLE_NOALLOC_SCRATCH_BYTES (16u << 20)

@@ -261,21 +261,22 @@ def test_attention_parity_70b_gqa_layer(lib, orc):
     say(f"  all 61 x 64 (row, head) outputs: worst |o - oracle| = {worst:.2e}")
 
 
-@pytest.mark.skip(reason="faulted the GPU (memory aperture violation) with an earlier bf16 attention kernel "
-                         "whose workgroups walked across sequences; the cause was not shown, so this case "
-                         "stays off the GPU this round (the kernel now runs one sequence per launch)")
 def test_attention_parity_batched_ragged_sampled(lib, orc):
+    """The batched workload's attention as the library runs it: one call over the 16
+    packed ragged sequences (contexts 512-16384, about 136k cache rows), all of them
+    in one kernel launch; sampled outputs and lse of every sequence against the
+    oracle.  (The launch plan of this exact descriptor is checked in bounds on the
+    host by tests/test_attn_plan.py.)"""
     eb, stepm, wl = lib
     w = wl.CONFIGS["batched_13b"]
-    say("[attention parity] batched_13b, 1 layer, 16 ragged sequences, sampled outputs")
+    say("[attention parity] batched_13b, 1 layer, 16 ragged sequences in one call, sampled outputs")
     vs = stepm.VerifyStep(w, layers=1)
     vs.tree(); vs.attention()
     torch.cuda.synchronize()
     trees = oracle_trees(orc, w, vs.draft_np, vs.root_np, vs.ctx_lens_np)
-    lens = vs.ctx_lens_np
-    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3, 11})
-    attention_check(orc, vs, trees, 0, 40, seqs=seqs)
+    attention_check(orc, vs, trees, 0, 30)
     assert torch.isfinite(vs.attn[0]["o"].float()).all()
+    same_without_host_lengths(eb, vs)
 
 
 def test_attention_parity_batched_sequences_one_by_one(lib, orc):
