@@ -219,7 +219,9 @@ struct AttnArgs {
     int64_t kv_rows_total;
     int B, T, Hq, Hkv, G, RG;
     float scale_log2;
-    HostPlan hp;               // kHostLen only
+    int32_t one_S;             // kOne: the one sequence's keys (ctx + T) and first row
+    int64_t one_row0;
+    HostPlan hp;               // kHostTab only
 };
 
 // The per-sequence table, as the plan functions read it: from the launch
@@ -230,6 +232,16 @@ struct ArgTab {
     __host__ __device__ int64_t row0(int b) const { return hp->row0[b]; }
     __host__ __device__ uint32_t cost0(int b) const { return hp->cost0[b]; }
     __host__ __device__ int64_t key0(int b) const { return hp->key0[b]; }
+};
+// One sequence whose length the host knows: every entry from two scalar arguments.
+struct OneTab {
+    int32_t S0;
+    int64_t r0;
+    int UPS;
+    __device__ int S(int) const { return S0; }
+    __device__ int64_t row0(int) const { return r0; }
+    __device__ uint32_t cost0(int b) const { return b == 0 ? 0u : (uint32_t)UPS * plan::unit_cost(S0); }
+    __device__ int64_t key0(int b) const { return b == 0 ? 0 : (int64_t)UPS * S0; }
 };
 struct LdsTab {
     const int32_t* s;
@@ -738,10 +750,12 @@ __device__ __forceinline__ void build_table(const int32_t* ctx_len, const int64_
     }
 }
 
-// One launch covers B <= plan::kMaxSeqs sequences.  kHostLen: the host computed
-// the launch plan (B <= kArgSeqs), read from the launch arguments; otherwise the
-// kernel reads the lengths and builds the plan itself.
-template <bool kHostLen>
+// One launch covers B <= plan::kMaxSeqs sequences.  The per-sequence table comes
+// from the host (kHostTab: up to kArgSeqs sequences, in the launch arguments;
+// kOne: one sequence, two scalar arguments) or is built by the kernel from the
+// device arrays of lengths and first rows.
+constexpr int kDevTab = 0, kHostTab = 1, kOne = 2;
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
@@ -762,7 +776,17 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         else
             tile_loop<false>(a, tab, smem, qslot, mslot, s_ml, wid, lane, vwg, len, tb);
     };
-    if constexpr (kHostLen) {
+    if constexpr (kMode == kOne) {
+        const OneTab tab{a.one_S, a.one_row0, UPS};
+        const Split sp = plan::make_split(tab.cost0(1), (int)gridDim.x, UPS);
+        const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
+        if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
+        const Pos tb = plan::split_tile(tab, 1, UPS, plan::stretch_start(sp, vwg));
+        const Pos te = plan::split_tile(tab, 1, UPS, plan::stretch_start(sp, vwg + 1));
+        const int64_t x_begin = plan::key_index(tab, 1, tb), x_end = plan::key_index(tab, 1, te);
+        if (x_begin >= x_end) return;  // a stretch in the steps before a unit's first tile
+        walk(tab, vwg, (int)(x_end - x_begin), tb);
+    } else if constexpr (kMode == kHostTab) {
         const ArgTab tab{&a.hp};
         const Split sp = plan::make_split(a.hp.cost0[B], (int)gridDim.x, B * UPS);
         const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
@@ -1146,14 +1170,20 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         hipError_t e;
         if (host) {
             const int merge_wg = host_plan(a.hp, m.mp, d.ctx_len_host + b0, d.kv_row_off_host + b0, nb, d.T, UPS);
-            tree_attn_bf16_kernel<true><<<kGridWG, kThreads, 0, stream>>>(a);  // 4 computing waves + 4 loaders
+            a.one_S = a.hp.S[0];
+            a.one_row0 = a.hp.row0[0];
+            // 4 computing waves + 4 loaders per workgroup
+            if (nb == 1)
+                tree_attn_bf16_kernel<kOne><<<kGridWG, kThreads, 0, stream>>>(a);
+            else
+                tree_attn_bf16_kernel<kHostTab><<<kGridWG, kThreads, 0, stream>>>(a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (merge_wg > 0)
                 tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(m);
             else if (merge_wg < 0)
                 tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
         } else {
-            tree_attn_bf16_kernel<false><<<kGridWG, kThreads, 0, stream>>>(a);
+            tree_attn_bf16_kernel<kDevTab><<<kGridWG, kThreads, 0, stream>>>(a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
         }

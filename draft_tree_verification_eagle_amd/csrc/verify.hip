@@ -281,7 +281,6 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
     __shared__ RowStats s_rs[EAGLE_MAX_TREE_ROWS];
     __shared__ int32_t s_tok[EAGLE_MAX_TREE_ROWS];
     __shared__ int32_t s_par[EAGLE_MAX_TREE_ROWS];
-    __shared__ int32_t s_first[EAGLE_MAX_TREE_ROWS];  // 1: no earlier sibling carries the row's token
     __shared__ int32_t s_path[kMaxDepth];      // depth <= 255: accepted rows, -1 padded
     __shared__ int32_t s_out[kMaxDepth + 1];   // accepted tokens then the bonus, -1 padded
     __shared__ int s_bonus_row, s_len;
@@ -309,13 +308,6 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
         if (tid <= depth) s_out[tid] = -1;
     }
     __syncthreads();
-    if (tid < T) {
-        int first = 1;
-        for (int j = 1; j < tid; ++j)
-            if (s_par[j] == s_par[tid] && s_tok[j] == s_tok[tid]) first = 0;
-        s_first[tid] = first;
-    }
-    __syncthreads();
 
     // The walk, by wave 0: lane j evaluates row j when it is a child of the
     // current row; its slot is its index among the row's children (flattened
@@ -326,6 +318,15 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
     // `rest`) and the tokens whose first carrier among the children is c or later;
     // a child whose token an earlier sibling carried has probability 0.
     if (tid < kWave) {
+        // bit j: no earlier sibling of row j carries row j's token (each row's parent
+        // and token broadcast to the wave in turn)
+        const int my_par = lane < T ? s_par[lane] : -2, my_tok = lane < T ? s_tok[lane] : -1;
+        bool first = lane < T;
+        for (int i = 1; i < T; ++i) {
+            const int pi = __builtin_amdgcn_readlane(my_par, i), ti = __builtin_amdgcn_readlane(my_tok, i);
+            if (i < lane && pi == my_par && ti == my_tok) first = false;
+        }
+        const uint64_t firsts = __ballot(first);
         int cur = 0, len = 0;
         while (true) {
             const RowStats& R = s_rs[cur];
@@ -339,11 +340,11 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
                         pass = s_tok[lane] == R.argmax;
                     } else {
                         double denom = ((R.rest[0] + R.rest[1]) + R.rest[2]) + R.rest[3];
-                        for (uint64_t m = kids >> lane; m; m &= m - 1) {
+                        for (uint64_t m = (kids & firsts) >> lane; m; m &= m - 1) {
                             const int j = lane + __ffsll((unsigned long long)m) - 1;
-                            if (s_first[j]) denom += s_rs[j].e_kid;
+                            denom += s_rs[j].e_kid;
                         }
-                        const double ratio = s_first[lane] ? s_rs[lane].e_kid / denom : 0.0;
+                        const double ratio = ((firsts >> lane) & 1) ? s_rs[lane].e_kid / denom : 0.0;
                         const int slot = __popcll(kids & ((1ull << lane) - 1ull));
                         const double u = decision_uniform(seed, step, (uint32_t)b, (uint32_t)cur, (uint32_t)slot);
                         pass = u < ratio;
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
             }
             // every child of the final row was tested and rejected (none when it is a
             // leaf, or when the path has reached the depth limit): its distinct tokens
-            const bool rem = len < depth && is_kid && s_first[lane];
+            const bool rem = len < depth && is_kid && ((firsts >> lane) & 1);
             const uint64_t rbal = __ballot(rem);
             if (rem) {
                 const int c = __popcll(rbal & ((1ull << lane) - 1ull));
