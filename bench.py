@@ -266,6 +266,8 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
         moved += len(path) - stay
     vs.accept_len.copy_(torch.from_numpy(al)); vs.accept_path.copy_(torch.from_numpy(ap))
     rope_us = _graph_us(lambda: vs.rope(), 2) / vs.n_layers
+    attn_us = _graph_us(lambda: vs.attention(), 2) / vs.n_layers
+    attn_rope_us = _graph_us(lambda: vs.attention_rope(), 2) / vs.n_layers
     rope_bytes = 2 * (w.batch * w.T * w.n_q_heads + w.batch * w.T * w.n_kv_heads) * w.head_dim * elt
     commit_us = _graph_us(lambda: vs.commit(), reps)
     commit_bytes = 2 * 2 * vs.n_layers * w.n_kv_heads * w.head_dim * elt * moved
@@ -275,21 +277,31 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
 
     draft = _time_draft_side(vs, w, stream)
 
-    def decode_step():
+    def decode_step_fused():
+        vs.tree()
+        vs.attention_rope()
+        vs.verify(temperature, seed, 0)
+        vs.commit()
+
+    def decode_step_separate():
         vs.tree()
         vs.rope()
         vs.attention()
         vs.verify(temperature, seed, 0)
         vs.commit()
-    decode_step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        decode_step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    full_us = e0.elapsed_time(e1) * 1e3 / 10
+
+    def eager_us(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    full_us = eager_us(decode_step_fused)
+    separate_us = eager_us(decode_step_separate)
     return {
         "rope": {"us_per_layer_call": round(rope_us, 3), "bytes_per_call": rope_bytes,
                  "GBps": round(rope_bytes / (rope_us * 1e-6) / 1e9, 1),
@@ -299,13 +311,21 @@ def time_extras(vs, w, stream, temperature, seed, reps: int = 20):
                       "GBps": round(commit_bytes / (commit_us * 1e-6) / 1e9, 1) if commit_bytes else None,
                       "what": f"K and V of the accepted rows moved behind the context in all {vs.n_layers} "
                               f"layers (path: the deepest root path of the tree)"},
+        "attention_rope": {"us_per_layer_call": round(attn_rope_us, 3),
+                           "attention_alone_us": round(attn_us, 3),
+                           "added_us": round(attn_rope_us - attn_us, 3),
+                           "what": "one layer's tree attention with the rotary at the tree positions inside it "
+                                   "(eagle_tree_attention_rope), against the same call without rotary"},
         "mask_static": {"us_per_call": round(static_us, 3)},
         "draft_side": draft,
         "timing": "graph replays of the calls, HIP events",
         "decode_step_with_rope_and_commit": {
             "ms": round(full_us / 1e3, 4), "steps_per_s": round(1e6 / full_us, 2),
-            "what": "expand x depth + rerank + mask + (rotary + attention) x layers + verify + KV commit, "
+            "what": "expand x depth + rerank + mask + attention with rotary inside x layers + verify + KV commit, "
                     "eager launches"},
+        "decode_step_with_separate_rope_call": {
+            "ms": round(separate_us / 1e3, 4), "steps_per_s": round(1e6 / separate_us, 2),
+            "what": "the same step with eagle_tree_rope called before plain attention in every layer"},
     }
 
 

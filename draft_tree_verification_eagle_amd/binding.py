@@ -61,6 +61,8 @@ def load_library(path: str = _LIB_PATH) -> C.CDLL:
     L.eagle_tree_mask.argtypes = [P, P, P, P, P, P, P, P, P, P]; L.eagle_tree_mask.restype = C.c_int
     L.eagle_tree_attention_workspace.argtypes = [P]; L.eagle_tree_attention_workspace.restype = sz
     L.eagle_tree_attention.argtypes = [P, P, P, P, P, P, P, P, sz, P]; L.eagle_tree_attention.restype = C.c_int
+    L.eagle_tree_attention_rope.argtypes = [P, P, C.c_double, P, P, P, P, P, P, P, sz, P]
+    L.eagle_tree_attention_rope.restype = C.c_int
     L.eagle_tree_attention_noalloc.argtypes = [P, P, P, P, P, P, P, P]
     L.eagle_tree_attention_noalloc.restype = C.c_int
     L.eagle_verify_workspace.argtypes = [P]; L.eagle_verify_workspace.restype = sz
@@ -199,6 +201,14 @@ def eagle_tree_attention(desc: AttnDesc, q, k_cache, v_cache, mask, o, lse, work
     _check("eagle_tree_attention", _lib.eagle_tree_attention(
         C.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(mask), _ptr(o), _ptr(lse),
         _ptr(workspace), nbytes, _stream(stream)))
+
+
+def eagle_tree_attention_rope(desc: AttnDesc, position, base: float, q, k_cache, v_cache, mask, o, lse, workspace,
+                              stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("eagle_tree_attention_rope", _lib.eagle_tree_attention_rope(
+        C.byref(desc), _ptr(position), float(base), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(mask), _ptr(o),
+        _ptr(lse), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def eagle_tree_attention_noalloc(desc: AttnDesc, q, k_cache, v_cache, mask, o, lse, stream=None):

@@ -154,6 +154,22 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
     return from_hip(eagle::launch_attention(*desc, q, k_cache, v_cache, mask, o, lse, workspace, stream));
 }
 
+int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* position, double base, const void* q,
+                              void* k_cache, const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int st = attn_desc_check(desc);
+    if (st != EAGLE_OK) return st;
+    if (desc->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
+    if (!(base > 0.0) || isinf(base)) return EAGLE_ERR_INVALID_ARG;
+    if (desc->batch == 0) return EAGLE_OK;
+    if (!position || !q || !k_cache || !v_cache || !mask || !o || !desc->ctx_len || !desc->kv_row_off)
+        return EAGLE_ERR_INVALID_ARG;
+    const size_t need = eagle::attention_workspace_bytes(*desc);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return EAGLE_ERR_WORKSPACE;
+    return from_hip(eagle::launch_attention(*desc, q, k_cache, v_cache, mask, o, lse, workspace, stream, position,
+                                            base));
+}
+
 int eagle_tree_attention_noalloc(const eagle_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const uint64_t* mask, void* o, float* lse,
                                  hipStream_t stream) {

@@ -221,6 +221,8 @@ struct AttnArgs {
     float scale_log2;
     int32_t one_S;             // kOne: the one sequence's keys (ctx + T) and first row
     int64_t one_row0;
+    const int32_t* rope_pos;   // kRope: tree rows' positions [B][T]
+    double rope_turns[kD / 2]; // kRope: base^(-2d/D) / (2 pi), turns per position
     HostPlan hp;               // kHostTab only
 };
 
@@ -332,13 +334,97 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, const Tile& t, unsigne
     }
 }
 
+// Rotary inside the attention kernel (kRope).  A tree's rows sit at a few
+// positions (the context length plus the row's depth), so each workgroup keeps in
+// LDS the fp32 (cos, sin) of every pair d < 64 at kRopeTab consecutive positions
+// lo .. lo + kRopeTab - 1 (a window).  At a rotation (q rows at a segment start,
+// the tree rows' K when their tile lands) the rows are taken window by window:
+// lo = the smallest position of the sequence, then the smallest position at or
+// past lo + kRopeTab, and so on; one window covers any tree of depth below
+// kRopeTab.  q rows are rotated in registers, K rows in LDS.
+constexpr int kRopeTab = 8;
+struct RopeLds {
+    float2* cs;     // [kRopeTab][64] (cos, sin) at lo + j, pair d
+    int32_t* pos;   // [4][64] positions of the tree rows, sequence b in ring slot b & 3
+    double* f;      // [64] turns per position of pair d
+    int32_t* info;  // [2] the first sequence's smallest position, and whether one window misses a row
+};
+// Rotation of the pair (x[e], y[e]) by (c, sn), rounded to bf16.
+__device__ __forceinline__ void rope_pair(bf16x8& x, bf16x8& y, int e, float c, float sn) {
+    const float xf = (float)x[e], yf = (float)y[e];
+    x[e] = (__bf16)(xf * c - yf * sn);
+    y[e] = (__bf16)(yf * c + xf * sn);
+}
+// q: this lane's row, at table row j, dims 16 kk + 8 h2 + e (kk < 8, e < 8) in
+// q[kk][e]; pair (d, d + 64) is (q[kk][e], q[kk + 4][e]).
+__device__ __forceinline__ void rope_q_regs(const RopeLds& r, int j, int h2, bf16x8 (&q)[8]) {
+    const float4* t = reinterpret_cast<const float4*>(r.cs) + j * (kD / 4) + 4 * h2;
+    float4 v[4];  // pairs 16 kk + 8 h2 + 2 x, + 1 in v[x]
+#pragma unroll
+    for (int x = 0; x < 4; ++x) v[x] = t[x];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        float4 nv[4];  // the next kk's entries, loading while these pairs rotate
+        if (kk < 3) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) nv[x] = t[8 * (kk + 1) + x];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            rope_pair(q[kk], q[kk + 4], 2 * x, v[x].x, v[x].y);
+            rope_pair(q[kk], q[kk + 4], 2 * x + 1, v[x].z, v[x].w);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk < 3) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) v[x] = nv[x];
+        }
+    }
+}
+// K: one LDS row of a tile at table row j, logical chunk c < 8 and its partner
+// chunk c + 8 (16-byte chunks at positions chunk ^ sw).
+__device__ __forceinline__ void rope_k_lds(const RopeLds& r, int j, unsigned char* row, int c, int sw) {
+    bf16x8* px = (bf16x8*)(row + ((c ^ sw) << 4));
+    bf16x8* py = (bf16x8*)(row + (((c + 8) ^ sw) << 4));
+    bf16x8 vx = *px, vy = *py;
+    const float4* t = reinterpret_cast<const float4*>(r.cs) + j * (kD / 4) + 4 * c;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const float4 v = t[x];
+        rope_pair(vx, vy, 2 * x, v.x, v.y);
+        rope_pair(vx, vy, 2 * x + 1, v.z, v.w);
+    }
+    *px = vx;
+    *py = vy;
+}
+// Loader wave li == 0: the T positions of sequence b into LDS (lane l reads row
+// min(l, T - 1)).
+__device__ __forceinline__ void load_pos(const AttnArgs& a, int b, int32_t* dst, int li, int lane) {
+    if (li != 0) return;
+    vm_wait<62>();
+    const int i = lane < a.T ? lane : a.T - 1;
+    dma_b32(a.rope_pos + (int64_t)b * a.T + i, lds_u32(dst));
+}
+// Minimum over the wave, in every lane: row (16-lane) prefix minima by DPP row
+// shifts (a lane with no source keeps its own value), then the rows' last lanes
+// broadcast into the rows after them; lane 63 ends with the minimum.
+__device__ __forceinline__ int wave_min(int x) {
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false));  // row_bcast:15 into rows 1, 3
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false));  // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
 // The tile walk of one workgroup, for the loader wave (kLoader) or a computing
 // wave.  Both instantiations share every branch that reaches a barrier, so the
 // five waves always meet the same barriers in the same order.
-template <bool kLoader, class Tab>
+template <bool kLoader, bool kRope, class Tab>
 __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, unsigned char* smem,
                                           unsigned char* qslot, uint32_t* mslot, float (*s_ml)[2][2][kWave],
-                                          int wid, int lane, int vwg, int len, Pos tb) {
+                                          const RopeLds& rl, int wid, int lane, int vwg, int len, Pos tb) {
     constexpr bool loader = kLoader;
     const int rb = wid & 1, ks = (wid >> 1) & 1;
     const int l32 = lane & 31, h2 = lane >> 5;
@@ -358,6 +444,82 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
     const int qrow = 32 * rb + l32;  // this lane's packed query row inside the unit
     bf16x8 qcur[8];
     uint64_t mword_n;
+    // Rotary (kRope): the (cos, sin) table holds the window at rt_lo of sequence
+    // rt_b.  For sequence rs_b the smallest position rs_min, and rs_multi: whether
+    // a row lies past the first window.  Positions of the sequences after the
+    // first ride into LDS with the loads (pos_b: the last sequence whose positions
+    // were requested).
+    constexpr int64_t kNoWindow = INT64_MIN;
+    int64_t rt_lo = kNoWindow;
+    int rt_b = tb.b, rs_b = tb.b, rs_min = 0, pos_b = tb.b;
+    bool rs_multi = false;
+    auto build_window = [&](int64_t lo, double f) {  // computing waves; a barrier follows
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = wid + 4 * h;
+            const int64_t pj = lo + j;
+            float c, sn;
+            rope_cs_turns(pj > INT_MAX ? INT_MAX : (int)pj, f, c, sn);
+            rl.cs[j * (kD / 2) + lane] = make_float2(c, sn);
+        }
+    };
+    // One rotation, run by every wave (the same barriers); the computing waves
+    // rotate the q rows of tile t's unit in registers (q_ev) and the tree rows of
+    // tile t's K in stage st (k_ev), one window at a time.
+    auto rope_event = [&](const Tile& t, bool q_ev, bool k_ev, unsigned char* st, bool q_known = false,
+                          int q_known_pos = 0) {
+        const int32_t* sp = rl.pos + (t.b & 3) * kWave;
+        if (t.b != rs_b) {  // another sequence (its positions are in LDS)
+            const int p = lane < T ? sp[lane] : INT_MAX;
+            rs_min = wave_min(p);
+            rs_multi = __any(lane < T && (int64_t)p >= (int64_t)rs_min + kRopeTab);
+            rs_b = t.b;
+        }
+        int64_t lo = rs_min;
+        int qpos = q_known_pos;
+        if (!loader && q_ev && !q_known) {
+            int i, hq;
+            query_row(a, t.g, t.rg * kUnitRows + qrow, i, hq);
+            qpos = sp[i];
+        }
+        const int ctx = t.S - T;
+        for (;;) {
+            if (lo != rt_lo || t.b != rt_b) {
+                if (!loader) build_window(lo, rl.f[lane]);
+                rt_lo = lo;
+                rt_b = t.b;
+                barrier_lds();
+            }
+            if (!loader) {
+                if (q_ev) {
+                    const int64_t j = qpos - lo;
+                    if (j >= 0 && j < kRopeTab) rope_q_regs(rl, (int)j, h2, qcur);
+                }
+                if (k_ev) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        // computing thread t: (row, 16-byte chunk c < 8 with its partner c + 8)
+                        // for the two tasks t and t + 256
+                        const int task = h * 256 + wid * kWave + lane;
+                        const int r = task >> 3, c = task & 7;
+                        const int i = t.key0 + r - ctx;  // tree row
+                        if (r < t.nkeys && i >= 0) {
+                            const int64_t j = sp[i] - lo;
+                            if (j >= 0 && j < kRopeTab) rope_k_lds(rl, (int)j, st + r * kRowBytes, c, swz(r));
+                        }
+                    }
+                }
+            }
+            if (!rs_multi) break;
+            // the next window: the smallest position at or past lo + kRopeTab
+            const int p = lane < T ? sp[lane] : 0;
+            const bool later = lane < T && p >= lo + kRopeTab;
+            if (!__any(later)) break;
+            lo = wave_min(later ? p : INT_MAX);
+            barrier_lds();  // every wave is done with this window before it is replaced
+        }
+        if (k_ev) barrier_lds();
+    };
     auto load_q_direct = [&](const Tile& t) {
         int i, hq;
         query_row(a, t.g, t.rg * kUnitRows + qrow, i, hq);
@@ -389,7 +551,32 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
     // keeps the slot free from the start for the next segment's Q, which rides with
     // that segment's first tile (a third segment starting while the slot is still
     // busy loads its Q directly when its scores are computed).
-    if (!loader) load_q_direct(plan::peek(w0, len));
+    int qpos0 = 0;  // kRope: the position of this lane's first q row
+    if (!loader) {
+        if (kRope) {
+            const Tile t0 = plan::peek(w0, len);
+            int i0, hq0;
+            query_row(a, t0.g, t0.rg * kUnitRows + qrow, i0, hq0);
+            const int p0 = lane < T ? a.rope_pos[(int64_t)tb.b * T + lane] : 0;
+            qpos0 = a.rope_pos[(int64_t)tb.b * T + i0];
+            const double f0 = a.rope_turns[lane];
+            load_q_direct(t0);
+            rs_min = wave_min(lane < T ? p0 : INT_MAX);
+            rs_multi = __any(lane < T && (int64_t)p0 >= (int64_t)rs_min + kRopeTab);
+            if (wid == 0) {
+                rl.pos[(tb.b & 3) * kWave + lane] = p0;
+                rl.f[lane] = f0;
+                if (lane == 0) {
+                    rl.info[0] = rs_min;
+                    rl.info[1] = rs_multi ? 1 : 0;
+                }
+            }
+            build_window(rs_min, f0);
+            rt_lo = rs_min;
+        } else {
+            load_q_direct(plan::peek(w0, len));
+        }
+    }
     auto fetch = [&]() {
         const Tile t = plan::peek(wf, len);
         if (loader)
@@ -400,9 +587,23 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
         }
         plan::advance(wf, t.nkeys, tab, B, a.RG, UPS);
         ++nl;
+        // the next sequence's positions ride with the last tile before it
+        if (kRope && wf.x < len && wf.b != pos_b) {
+            pos_b = wf.b;
+            if (loader) load_pos(a, wf.b, rl.pos + (wf.b & 3) * kWave, wid - kComputeWaves, lane);
+        }
     };
     fetch();
     if (wf.x < len) fetch();
+    if (kRope) {
+        barrier_lds();  // the first sequence's positions and first window are in LDS
+        if (loader) {
+            rs_min = uni(rl.info[0]);
+            rs_multi = uni(rl.info[1]) != 0;
+            rt_lo = rs_min;
+        }
+        rope_event(plan::peek(w0, len), true, false, nullptr, true, qpos0);
+    }
     // tile 0's K; its V and tile 1 (with any Q that rode with it) may still be in
     // flight, since the first iteration's barrier waits for them.  A one-tile
     // stretch has no such barrier: there everything must land here.
@@ -434,6 +635,8 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
     Walker wn = w0;           // tile whose scores are computed next
     Tile tc = plan::peek(wn, len);
     plan::advance(wn, tc.nkeys, tab, B, a.RG, UPS);
+    if (kRope && tc.key0 + tc.nkeys > tc.S - T)  // tree rows in tile 0 (its K has landed)
+        rope_event(tc, false, true, smem);
     f32x16 sacc;
     if (!loader) sacc = scores(smem);
     uint64_t mword_c = mword_n;
@@ -460,15 +663,18 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             tn = plan::peek(wn, len);
             if (tn.seg_start) {
                 if (q_slot_tile == it + 1) {
-                    if (!loader) {
-                        read_q_slot();
-                    }
+                    if (!loader) read_q_slot();
                     q_slot_tile = -1;  // free once every wave has passed the next barrier
                 } else if (!loader) {
                     load_q_direct(tn);  // rare (short segments)
                 }
                 from0_n = tn.key0 == 0;
             }
+            // q rows at a segment start, the tree rows of the tile just landed (a new
+            // sequence's positions landed with an earlier tile)
+            const bool k_tree = kRope && tn.key0 + tn.nkeys > tn.S - T;
+            if (kRope && (tn.seg_start || k_tree))
+                rope_event(tn, tn.seg_start, k_tree, smem + ((it + 1) % kStages) * kStageBytes);
         }
 
         f32x16 snext;
@@ -755,12 +961,17 @@ __device__ __forceinline__ void build_table(const int32_t* ctx_len, const int64_
 // kOne: one sequence, two scalar arguments) or is built by the kernel from the
 // device arrays of lengths and first rows.
 constexpr int kDevTab = 0, kHostTab = 1, kOne = 2;
-template <int kMode>
+template <int kMode, bool kRope>
 __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char qslot[kQBytes];
     __shared__ uint32_t mslot[2 * kWave];
     __shared__ float s_ml[2][2][2][kWave];  // [key half][query half][max, sum][lane]
+    __shared__ __attribute__((aligned(16))) float2 s_rcs[kRope ? kRopeTab * kD / 2 : 2];
+    __shared__ int32_t s_rpos[kRope ? 4 * kWave : 1];
+    __shared__ double s_rf[kRope ? kD / 2 : 1];
+    __shared__ int32_t s_rinfo[2];
+    const RopeLds rl{s_rcs, s_rpos, s_rf, s_rinfo};
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -772,9 +983,9 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
     // roles run the same tile walk and the same barriers.
     auto walk = [&](const auto& tab, int vwg, int len, const Pos& tb) {
         if (wid >= kComputeWaves)
-            tile_loop<true>(a, tab, smem, qslot, mslot, s_ml, wid, lane, vwg, len, tb);
+            tile_loop<true, kRope>(a, tab, smem, qslot, mslot, s_ml, rl, wid, lane, vwg, len, tb);
         else
-            tile_loop<false>(a, tab, smem, qslot, mslot, s_ml, wid, lane, vwg, len, tb);
+            tile_loop<false, kRope>(a, tab, smem, qslot, mslot, s_ml, rl, wid, lane, vwg, len, tb);
     };
     if constexpr (kMode == kOne) {
         const OneTab tab{a.one_S, a.one_row0, UPS};
@@ -825,7 +1036,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
 constexpr int kRowBlocks = kUnitRows / 16;
-constexpr int kPlanWgs = 384;  // merge workgroups a host plan covers (96 split units)
+constexpr int kPlanWgs = 256;  // merge workgroups a host plan covers (64 split units)
 // Per merge workgroup: bit 63 set = in use, then b (bits 0..15), uis (16..39), vf
 // (40..47), vl (48..55), row block (56..57); read by workgroup index alone.
 struct MergePlan {
@@ -839,12 +1050,62 @@ struct MergeArgs {
     const int32_t* ctx_len;
     const int64_t* kv_row_off;
     int B, T, Hq, Hkv, G, RG;
-    MergePlan mp;  // kHostPlan only
+    int n_merge;                 // workgroups of the merge proper; kRope: the rest rotate the cache
+    // kRope: the tree rows' K in the cache, rotated in place as the rotary call does
+    uint16_t* k;
+    int64_t kv_rows_total;
+    const int32_t* rope_pos;     // [B][T]
+    double rope_f[kD / 2];       // base^(-2d/D)
+    int64_t krow_h[kArgSeqs];    // with a host plan: sequence b's first tree row
+    MergePlan mp;                // kHostPlan only
 };
 
+// kRope: the K of the tree rows in the cache rotated in place, with the rotary
+// call's arithmetic (fp64 angle, cosine, sine and rotation; fp32, then bf16), so
+// the cache ends as that call leaves it.  One workgroup per (tree row, sequence,
+// 16 KV heads); thread = (coordinate pair d < 64, every fourth head).  The main
+// kernel has read these rows unrotated (it rotates its own copies in LDS); this
+// kernel runs after it.
 template <bool kHostPlan>
+__device__ __forceinline__ void rope_cache_rows(const MergeArgs& m, int x) {
+    const int slices = (m.Hkv + 15) / 16;
+    const int i = x % m.T, rest = x / m.T;
+    const int slice = rest % slices, b = rest / slices;
+    const int d = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    const int64_t krow = kHostPlan ? m.krow_h[b] + i : m.kv_row_off[b] + (int64_t)m.ctx_len[b] + i;
+    if (krow < 0 || krow >= m.kv_rows_total) return;  // outside the cache: not rotated
+    const int pos = m.rope_pos[(int64_t)b * m.T + i];
+    uint16_t* rows[4];
+    double xv[4], yv[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int h = slice * 16 + grp + 4 * s4;
+        rows[s4] = h < m.Hkv ? m.k + ((int64_t)h * m.kv_rows_total + krow) * kD : nullptr;
+        if (rows[s4]) {
+            xv[s4] = (double)__uint_as_float((uint32_t)rows[s4][d] << 16);
+            yv[s4] = (double)__uint_as_float((uint32_t)rows[s4][d + 64] << 16);
+        }
+    }
+    double sn, cs;
+    sincos((double)pos * m.rope_f[d], &sn, &cs);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        if (rows[s4]) {
+            float xr, yr;
+            rope_rotate_f64(xv[s4], yv[s4], cs, sn, xr, yr);
+            rows[s4][d] = bf16_bits_rne(xr);
+            rows[s4][d + 64] = bf16_bits_rne(yr);
+        }
+    }
+}
+
+template <bool kHostPlan, bool kRope>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
     const int tid = threadIdx.x;
+    if (kRope && (int)blockIdx.x >= m.n_merge) {
+        rope_cache_rows<kHostPlan>(m, (int)blockIdx.x - m.n_merge);
+        return;
+    }
     int b, uis, vf, vl, rb;
     if constexpr (kHostPlan) {
         const uint64_t e = m.mp.e[blockIdx.x];
@@ -1120,8 +1381,9 @@ bool attention_split_fits(const eagle_attn_desc& d) {
 }
 
 hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k, const void* v,
-                            const uint64_t* mask, void* o, float* lse, void* workspace,
-                            hipStream_t stream) {
+                            const uint64_t* mask, void* o, float* lse, void* workspace, hipStream_t stream,
+                            const int32_t* rope_position, double rope_base) {
+    const bool rope = rope_position != nullptr;
     const float scale = d.scale != 0.0f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
     const int G = d.n_q_heads / d.n_kv_heads;
     if (d.dtype == EAGLE_F32) {
@@ -1157,6 +1419,7 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.kv_rows_total = d.kv_rows_total;
         a.B = nb; a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
         a.scale_log2 = scale * kLog2e;
+        a.rope_pos = rope ? rope_position + (size_t)b0 * d.T : nullptr;
         MergeArgs m;
         m.o = a.o;
         m.lse = a.lse;
@@ -1165,6 +1428,18 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         m.ctx_len = a.ctx_len;
         m.kv_row_off = a.kv_row_off;
         m.B = nb; m.T = d.T; m.Hq = d.n_q_heads; m.Hkv = d.n_kv_heads; m.G = G; m.RG = RG;
+        m.k = (uint16_t*)k;
+        m.kv_rows_total = d.kv_rows_total;
+        m.rope_pos = a.rope_pos;
+        if (rope) {
+            for (int j = 0; j < kD / 2; ++j) {
+                // the rotary call's frequencies, and the same in turns for the fp32 form
+                m.rope_f[j] = pow(rope_base, -2.0 * j / kD);
+                a.rope_turns[j] = m.rope_f[j] / (2.0 * M_PI);
+            }
+        }
+        // rotary write-back workgroups: (tree row, sequence, 16 KV heads)
+        const int rope_wg = rope ? d.T * nb * ((d.n_kv_heads + 15) / 16) : 0;
         // the merge plan packs (sequence, unit) in 16 + 24 bits
         const bool host = d.ctx_len_host && nb <= kArgSeqs && UPS < (1 << 24);
         hipError_t e;
@@ -1172,20 +1447,41 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
             const int merge_wg = host_plan(a.hp, m.mp, d.ctx_len_host + b0, d.kv_row_off_host + b0, nb, d.T, UPS);
             a.one_S = a.hp.S[0];
             a.one_row0 = a.hp.row0[0];
+            for (int b = 0; b < nb; ++b) m.krow_h[b] = a.hp.row0[b] + (a.hp.S[b] - d.T);
             // 4 computing waves + 4 loaders per workgroup
-            if (nb == 1)
-                tree_attn_bf16_kernel<kOne><<<kGridWG, kThreads, 0, stream>>>(a);
+            if (nb == 1 && rope)
+                tree_attn_bf16_kernel<kOne, true><<<kGridWG, kThreads, 0, stream>>>(a);
+            else if (nb == 1)
+                tree_attn_bf16_kernel<kOne, false><<<kGridWG, kThreads, 0, stream>>>(a);
+            else if (rope)
+                tree_attn_bf16_kernel<kHostTab, true><<<kGridWG, kThreads, 0, stream>>>(a);
             else
-                tree_attn_bf16_kernel<kHostTab><<<kGridWG, kThreads, 0, stream>>>(a);
+                tree_attn_bf16_kernel<kHostTab, false><<<kGridWG, kThreads, 0, stream>>>(a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            if (merge_wg > 0)
-                tree_attn_merge_kernel<true><<<merge_wg, 256, 0, stream>>>(m);
-            else if (merge_wg < 0)
-                tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
+            if (merge_wg >= 0) {
+                m.n_merge = merge_wg;
+                if (rope)
+                    tree_attn_merge_kernel<true, true><<<merge_wg + rope_wg, 256, 0, stream>>>(m);
+                else if (merge_wg > 0)
+                    tree_attn_merge_kernel<true, false><<<merge_wg, 256, 0, stream>>>(m);
+            } else {
+                m.n_merge = kRowBlocks * kGridWG;
+                if (rope)
+                    tree_attn_merge_kernel<false, true><<<m.n_merge + rope_wg, 256, 0, stream>>>(m);
+                else
+                    tree_attn_merge_kernel<false, false><<<m.n_merge, 256, 0, stream>>>(m);
+            }
         } else {
-            tree_attn_bf16_kernel<kDevTab><<<kGridWG, kThreads, 0, stream>>>(a);
+            if (rope)
+                tree_attn_bf16_kernel<kDevTab, true><<<kGridWG, kThreads, 0, stream>>>(a);
+            else
+                tree_attn_bf16_kernel<kDevTab, false><<<kGridWG, kThreads, 0, stream>>>(a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            tree_attn_merge_kernel<false><<<kRowBlocks * kGridWG, 256, 0, stream>>>(m);
+            m.n_merge = kRowBlocks * kGridWG;
+            if (rope)
+                tree_attn_merge_kernel<false, true><<<m.n_merge + rope_wg, 256, 0, stream>>>(m);
+            else
+                tree_attn_merge_kernel<false, false><<<m.n_merge, 256, 0, stream>>>(m);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

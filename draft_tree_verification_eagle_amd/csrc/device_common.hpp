@@ -239,6 +239,33 @@ __device__ __forceinline__ double decision_uniform(uint64_t seed, uint64_t step,
 
 constexpr uint32_t kBonusSlot = 0xFFFFFFFFu;
 
+// ---------------------------------------------------------------------------
+// Rotary position encoding (half-split pairs).  The fp64 form: the pair (x, y)
+// rotated by an angle with cosine cs and sine sn, each product rounded (no fused
+// multiply-add), then rounded to fp32; bf16 storage rounds that to nearest even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_rotate_f64(double x, double y, double cs, double sn, float& xr, float& yr) {
+#pragma clang fp contract(off)
+    xr = (float)(x * cs - y * sn);
+    yr = (float)(y * cs + x * sn);
+}
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays a (quiet) NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+// The fp32 form used inside the attention kernel: cos and sin of pos * f, with
+// f_turns = f / (2 pi) the frequency in turns per position; the angle is taken
+// modulo one turn in fp64, and the hardware cosine and sine (which take turns)
+// of the remaining fraction give fp32 values.
+__device__ __forceinline__ void rope_cs_turns(int pos, double f_turns, float& c, float& s) {
+    const double t = (double)pos * f_turns;
+    const float fr = (float)(t - rint(t));  // in [-1/2, 1/2] turn
+    c = __builtin_amdgcn_cosf(fr);
+    s = __builtin_amdgcn_sinf(fr);
+}
+
 // Workgroup barrier that orders LDS traffic only: outstanding global loads and
 // stores stay in flight (__syncthreads would also wait for every store to complete).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

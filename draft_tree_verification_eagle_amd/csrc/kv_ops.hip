@@ -7,12 +7,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace eagle {
 namespace {
-
-constexpr int kWave = 64;  // lanes per wavefront
 
 // ---------------------------------------------------------------------------
 // Static tree: one wave per sequence, lane i = row i.  Row i's ancestors are
@@ -70,16 +69,8 @@ __device__ __forceinline__ double load_elt(const float* p) { return (double)*p; 
 __device__ __forceinline__ double load_elt(const uint16_t* p) {
     return (double)__uint_as_float((uint32_t)*p << 16);
 }
-__device__ __forceinline__ void store_elt(float* p, double x) { *p = (float)x; }
-__device__ __forceinline__ void store_elt(uint16_t* p, double x) {
-    uint32_t u = __float_as_uint((float)x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-        *p = (uint16_t)((u >> 16) | 0x40u);  // NaN stays a (quiet) NaN
-        return;
-    }
-    u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
-    *p = (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ void store_elt(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_elt(uint16_t* p, float x) { *p = bf16_bits_rne(x); }
 
 constexpr int kRopeHostRows = 32;  // sequences whose K row may ride in the launch arguments
 
@@ -134,8 +125,10 @@ __global__ __launch_bounds__(256) void rope_kernel(int T, int Hq, int Hkv, int D
 #pragma unroll
     for (int s = 0; s < kMaxPer; ++s) {
         if (rows[s]) {
-            store_elt(rows[s] + d, x[s] * cs - y[s] * sn);
-            store_elt(rows[s] + d + half, y[s] * cs + x[s] * sn);
+            float xr, yr;
+            rope_rotate_f64(x[s], y[s], cs, sn, xr, yr);
+            store_elt(rows[s] + d, xr);
+            store_elt(rows[s] + d + half, yr);
         }
     }
 }

@@ -31,9 +31,12 @@ size_t attention_workspace_bytes(const eagle_attn_desc& d);
 // The bf16 path splits its work on a 31-bit cost line; false if this shape would
 // not fit it.
 bool attention_split_fits(const eagle_attn_desc& d);
+// rope_position non-null: the bf16 attention of q and the tree K rows rotated at
+// those positions (rotary with base rope_base), the cache's tree K rows left rotated.
 hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void* k,
                             const void* v, const uint64_t* mask, void* o, float* lse,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream,
+                            const int32_t* rope_position = nullptr, double rope_base = 0.0);
 
 // The same launch with the partials in the library's per-device array of
 // EAGLE_NOALLOC_SCRATCH_BYTES (no caller workspace); the caller has checked the

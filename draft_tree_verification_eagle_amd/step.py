@@ -98,6 +98,14 @@ class VerifyStep:
             eb.eagle_tree_attention(self.desc, a["q"], a["k"], a["v"], self.mask, a["o"], a["lse"],
                                     self.attn_ws, stream)
 
+    def attention_rope(self, layers: Optional[Sequence[int]] = None, base: float = 10000.0, stream=None):
+        """Tree attention with the rotary at the tree positions applied inside it (q and
+        the K tree rows given unrotated; the cache's tree rows are left rotated)."""
+        for layer in (range(self.n_layers) if layers is None else layers):
+            a = self.attn[layer]
+            eb.eagle_tree_attention_rope(self.desc, self.position, base, a["q"], a["k"], a["v"], self.mask, a["o"],
+                                         a["lse"], self.attn_ws, stream)
+
     def verify(self, temperature: float, seed: int, step: int, stream=None):
         eb.eagle_verify(self.cfg, self.target, self.flat_token, self.flat_parent, temperature, seed, step,
                         self.accept_len, self.accept_path, self.out_tokens, self.verify_ws, stream)

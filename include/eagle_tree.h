@@ -11,6 +11,7 @@
  *   eagle_tree_mask_static  positions and ancestor mask of a caller-given fixed tree
  *                           (the static trees of EAGLE / Medusa), in place of the first three
  *   eagle_tree_rope         rotary position encoding of the tree rows at their positions
+ *   eagle_tree_attention_rope  tree attention with that rotary applied inside it
  *   eagle_kv_commit         move the accepted rows' K/V behind the context, as
  *                           autoregressive decoding would have left them
  *   eagle_draft_subtree     rows, masks and positions of the draft model's attention
@@ -193,6 +194,25 @@ size_t eagle_tree_attention_workspace(const eagle_attn_desc* desc);
 int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void* k_cache,
                          const void* v_cache, const uint64_t* mask, void* o, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Tree attention with rotary position encoding at the tree positions, in the
+ * same launches (EAGLE-2 page, passage after the two stages: each flattened
+ * token's position is adjusted to match plain autoregressive decoding).  The
+ * attention of eagle_tree_attention, with every q row and the K of every tree row
+ * rotated at its position (position [batch][T], from eagle_tree_mask or
+ * eagle_tree_mask_static) as eagle_tree_rope defines the rotation (half-split
+ * pairs, theta = p * base^(-2d / head_dim)); the context rows' K are used as
+ * stored (already rotated).  Inside the kernel the rotation takes fp32 cosines and
+ * sines of the angle reduced modulo one turn in fp64, so o and lse match
+ * eagle_tree_rope followed by eagle_tree_attention within the bf16 tolerance, not
+ * bit for bit.  Afterwards the tree rows' K in k_cache are rotated exactly as
+ * eagle_tree_rope(q = NULL) leaves them (so eagle_kv_commit applies unchanged);
+ * q is not modified, V is not touched.  BF16 only (F32 is EAGLE_ERR_UNSUPPORTED);
+ * base > 0 and finite; other arguments, limits and the workspace as
+ * eagle_tree_attention. */
+int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* position, double base, const void* q,
+                              void* k_cache, const void* v_cache, const uint64_t* mask, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Tree attention without a caller workspace, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses

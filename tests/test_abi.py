@@ -356,3 +356,35 @@ def test_noalloc_attention_validation(eb):
     assert L.eagle_tree_attention_noalloc(C.byref(d3), f, f, f, f, f, None, None) == eb.EAGLE_ERR_UNSUPPORTED
     d4 = eb.make_attn_desc(eb.EAGLE_BF16, 0, 16, 8, 8, 128, Dev(), Dev(), 4096)
     assert L.eagle_tree_attention_noalloc(C.byref(d4), f, f, f, f, f, None, None) == eb.EAGLE_OK  # empty batch
+
+
+def test_attention_rope_validation(eb):
+    """Tree attention with rotary: bf16 only, a position array and a positive
+    finite base, and the checks of the plain attention call, before any HIP call."""
+    L = eb.lib()
+
+    class Dev:
+        def data_ptr(self):
+            return 0x1000
+
+    f = 0x1000
+
+    def call(d, pos=f, base=10000.0, q=f, k=f, v=f, mask=f, o=f, ws=f, nbytes=1 << 30):
+        return L.eagle_tree_attention_rope(C.byref(d), pos, base, q, k, v, mask, o, None, ws, nbytes, None)
+
+    d = eb.make_attn_desc(eb.EAGLE_BF16, 1, 61, 40, 40, 128, Dev(), Dev(), 4157)
+    assert call(d, pos=None) == eb.EAGLE_ERR_INVALID_ARG
+    for base in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(d, base=base) == eb.EAGLE_ERR_INVALID_ARG
+    for arg in ("q", "k", "v", "mask", "o"):
+        assert call(d, **{arg: None}) == eb.EAGLE_ERR_INVALID_ARG
+    assert call(d, ws=None) == eb.EAGLE_ERR_WORKSPACE
+    assert call(d, nbytes=16) == eb.EAGLE_ERR_WORKSPACE
+    d32 = eb.make_attn_desc(eb.EAGLE_F32, 1, 61, 40, 40, 64, Dev(), Dev(), 4157)
+    assert call(d32) == eb.EAGLE_ERR_UNSUPPORTED
+    d96 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 61, 8, 8, 96, Dev(), Dev(), 4157)
+    assert call(d96) == eb.EAGLE_ERR_UNSUPPORTED
+    d0 = eb.make_attn_desc(eb.EAGLE_BF16, 0, 61, 40, 40, 128, Dev(), Dev(), 4157)
+    assert call(d0) == eb.EAGLE_OK  # empty batch
+    assert L.eagle_tree_attention_rope(None, f, 10000.0, f, f, f, f, f, None, f, 1 << 30, None) == \
+        eb.EAGLE_ERR_INVALID_ARG
