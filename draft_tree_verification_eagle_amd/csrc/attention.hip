@@ -337,11 +337,13 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, const Tile& t, unsigne
 // Rotary inside the attention kernel (kRope).  A tree's rows sit at a few
 // positions (the context length plus the row's depth), so each workgroup keeps in
 // LDS the fp32 (cos, sin) of every pair d < 64 at kRopeTab consecutive positions
-// lo .. lo + kRopeTab - 1 (a window).  At a rotation (q rows at a segment start,
-// the tree rows' K when their tile lands) the rows are taken window by window:
-// lo = the smallest position of the sequence, then the smallest position at or
-// past lo + kRopeTab, and so on; one window covers any tree of depth below
-// kRopeTab.  q rows are rotated in registers, K rows in LDS.
+// lo .. lo + kRopeTab - 1 (a window).  At a rotation (a unit's 64 q rows at a
+// segment start, the tree rows' K when their tile lands) the rows are taken window
+// by window: lo = the smallest position of the sequence, then the smallest
+// position at or past lo + kRopeTab, and so on; one window covers any tree of
+// depth below kRopeTab.  All rotation happens in LDS, by all eight waves, one
+// (row, 16-byte chunk pair) per thread: the q rows in the Q slot, or in a copy the
+// computing waves write when they loaded them directly.
 constexpr int kRopeTab = 8;
 struct RopeLds {
     float2* cs;     // [kRopeTab][64] (cos, sin) at lo + j, pair d
@@ -355,34 +357,8 @@ __device__ __forceinline__ void rope_pair(bf16x8& x, bf16x8& y, int e, float c, 
     x[e] = (__bf16)(xf * c - yf * sn);
     y[e] = (__bf16)(yf * c + xf * sn);
 }
-// q: this lane's row, at table row j, dims 16 kk + 8 h2 + e (kk < 8, e < 8) in
-// q[kk][e]; pair (d, d + 64) is (q[kk][e], q[kk + 4][e]).
-__device__ __forceinline__ void rope_q_regs(const RopeLds& r, int j, int h2, bf16x8 (&q)[8]) {
-    const float4* t = reinterpret_cast<const float4*>(r.cs) + j * (kD / 4) + 4 * h2;
-    float4 v[4];  // pairs 16 kk + 8 h2 + 2 x, + 1 in v[x]
-#pragma unroll
-    for (int x = 0; x < 4; ++x) v[x] = t[x];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        float4 nv[4];  // the next kk's entries, loading while these pairs rotate
-        if (kk < 3) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) nv[x] = t[8 * (kk + 1) + x];
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            rope_pair(q[kk], q[kk + 4], 2 * x, v[x].x, v[x].y);
-            rope_pair(q[kk], q[kk + 4], 2 * x + 1, v[x].z, v[x].w);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk < 3) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) v[x] = nv[x];
-        }
-    }
-}
-// K: one LDS row of a tile at table row j, logical chunk c < 8 and its partner
-// chunk c + 8 (16-byte chunks at positions chunk ^ sw).
+// One LDS row (q or K, 128 bf16 in 16-byte chunks at positions chunk ^ sw) at
+// table row j: logical chunk c < 8 and its partner chunk c + 8.
 __device__ __forceinline__ void rope_k_lds(const RopeLds& r, int j, unsigned char* row, int c, int sw) {
     bf16x8* px = (bf16x8*)(row + ((c ^ sw) << 4));
     bf16x8* py = (bf16x8*)(row + (((c + 8) ^ sw) << 4));
@@ -463,11 +439,11 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             rl.cs[j * (kD / 2) + lane] = make_float2(c, sn);
         }
     };
-    // One rotation, run by every wave (the same barriers); the computing waves
-    // rotate the q rows of tile t's unit in registers (q_ev) and the tree rows of
-    // tile t's K in stage st (k_ev), one window at a time.
-    auto rope_event = [&](const Tile& t, bool q_ev, bool k_ev, unsigned char* st, bool q_known = false,
-                          int q_known_pos = 0) {
+    // One rotation, run by every wave (the same barriers): the q rows of tile t's
+    // unit in q_buf (64 packed rows laid out as in the Q slot) and the tree rows of
+    // tile t's K in stage k_st, either may be null; a barrier ends it.  The caller
+    // has made q_buf's contents visible to every wave.
+    auto rope_event = [&](const Tile& t, unsigned char* q_buf, unsigned char* k_st) {
         const int32_t* sp = rl.pos + (t.b & 3) * kWave;
         if (t.b != rs_b) {  // another sequence (its positions are in LDS)
             const int p = lane < T ? sp[lane] : INT_MAX;
@@ -475,14 +451,18 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             rs_multi = __any(lane < T && (int64_t)p >= (int64_t)rs_min + kRopeTab);
             rs_b = t.b;
         }
-        int64_t lo = rs_min;
-        int qpos = q_known_pos;
-        if (!loader && q_ev && !q_known) {
+        const int task = wid * kWave + lane;  // (row r, chunk pair c) of 64 x 8
+        const int r = task >> 3, c = task & 7;
+        int qpos = 0, kpos = 0;
+        if (q_buf) {
             int i, hq;
-            query_row(a, t.g, t.rg * kUnitRows + qrow, i, hq);
+            query_row(a, t.g, t.rg * kUnitRows + r, i, hq);
             qpos = sp[i];
         }
-        const int ctx = t.S - T;
+        const int ki = t.key0 + r - (t.S - T);  // tree row of K row r
+        const bool k_act = k_st && r < t.nkeys && ki >= 0;
+        if (k_act) kpos = sp[ki];
+        int64_t lo = rs_min;
         for (;;) {
             if (lo != rt_lo || t.b != rt_b) {
                 if (!loader) build_window(lo, rl.f[lane]);
@@ -490,25 +470,12 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
                 rt_b = t.b;
                 barrier_lds();
             }
-            if (!loader) {
-                if (q_ev) {
-                    const int64_t j = qpos - lo;
-                    if (j >= 0 && j < kRopeTab) rope_q_regs(rl, (int)j, h2, qcur);
-                }
-                if (k_ev) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        // computing thread t: (row, 16-byte chunk c < 8 with its partner c + 8)
-                        // for the two tasks t and t + 256
-                        const int task = h * 256 + wid * kWave + lane;
-                        const int r = task >> 3, c = task & 7;
-                        const int i = t.key0 + r - ctx;  // tree row
-                        if (r < t.nkeys && i >= 0) {
-                            const int64_t j = sp[i] - lo;
-                            if (j >= 0 && j < kRopeTab) rope_k_lds(rl, (int)j, st + r * kRowBytes, c, swz(r));
-                        }
-                    }
-                }
+#pragma nounroll
+            for (int h = 0; h < 2; ++h) {
+                unsigned char* row = (h == 0 ? q_buf : k_st) + r * kRowBytes;
+                const int64_t j = (int64_t)(h == 0 ? qpos : kpos) - lo;
+                if ((h == 0 ? q_buf != nullptr : k_act) && j >= 0 && j < kRopeTab)
+                    rope_k_lds(rl, (int)j, row, c, swz(r));
             }
             if (!rs_multi) break;
             // the next window: the smallest position at or past lo + kRopeTab
@@ -518,7 +485,25 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             lo = wave_min(later ? p : INT_MAX);
             barrier_lds();  // every wave is done with this window before it is replaced
         }
-        if (k_ev) barrier_lds();
+        barrier_lds();
+    };
+    // computing waves of key half 0: this lane's q row into buf (the Q slot's layout)
+    auto write_q_rows = [&](unsigned char* buf) {
+        if (ks != 0) return;
+        const int qr = opaque(qrow), hh = opaque(h2);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int c = (2 * kk + hh) ^ swz(qr);
+            *(bf16x8*)(buf + qr * kRowBytes + c * 16) = qcur[kk];
+        }
+    };
+    auto read_q_rows = [&](const unsigned char* buf) {
+        const int qr = opaque(qrow), hh = opaque(h2);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int c = (2 * kk + hh) ^ swz(qr);
+            qcur[kk] = *(const bf16x8*)(buf + qr * kRowBytes + c * 16);
+        }
     };
     auto load_q_direct = [&](const Tile& t) {
         int i, hq;
@@ -532,12 +517,8 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
 
     // this lane's Q row and mask word from the Q slot
     auto read_q_slot = [&]() {
-        const int qr = opaque(qrow), hh = opaque(h2);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int c = (2 * kk + hh) ^ swz(qr);
-            qcur[kk] = *(const bf16x8*)(qslot + qr * kRowBytes + c * 16);
-        }
+        read_q_rows(qslot);
+        const int qr = opaque(qrow);
         mword_n = (uint64_t)mslot[qr] | ((uint64_t)mslot[kWave + qr] << 32);
     };
 
@@ -551,16 +532,11 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
     // keeps the slot free from the start for the next segment's Q, which rides with
     // that segment's first tile (a third segment starting while the slot is still
     // busy loads its Q directly when its scores are computed).
-    int qpos0 = 0;  // kRope: the position of this lane's first q row
     if (!loader) {
         if (kRope) {
-            const Tile t0 = plan::peek(w0, len);
-            int i0, hq0;
-            query_row(a, t0.g, t0.rg * kUnitRows + qrow, i0, hq0);
             const int p0 = lane < T ? a.rope_pos[(int64_t)tb.b * T + lane] : 0;
-            qpos0 = a.rope_pos[(int64_t)tb.b * T + i0];
             const double f0 = a.rope_turns[lane];
-            load_q_direct(t0);
+            load_q_direct(plan::peek(w0, len));
             rs_min = wave_min(lane < T ? p0 : INT_MAX);
             rs_multi = __any(lane < T && (int64_t)p0 >= (int64_t)rs_min + kRopeTab);
             if (wid == 0) {
@@ -573,6 +549,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             }
             build_window(rs_min, f0);
             rt_lo = rs_min;
+            write_q_rows(smem + 3 * kStageBytes);  // stage 3 is first filled in the loop
         } else {
             load_q_direct(plan::peek(w0, len));
         }
@@ -602,7 +579,8 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             rs_multi = uni(rl.info[1]) != 0;
             rt_lo = rs_min;
         }
-        rope_event(plan::peek(w0, len), true, false, nullptr, true, qpos0);
+        rope_event(plan::peek(w0, len), smem + 3 * kStageBytes, nullptr);
+        if (!loader) read_q_rows(smem + 3 * kStageBytes);
     }
     // tile 0's K; its V and tile 1 (with any Q that rode with it) may still be in
     // flight, since the first iteration's barrier waits for them.  A one-tile
@@ -636,7 +614,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
     Tile tc = plan::peek(wn, len);
     plan::advance(wn, tc.nkeys, tab, B, a.RG, UPS);
     if (kRope && tc.key0 + tc.nkeys > tc.S - T)  // tree rows in tile 0 (its K has landed)
-        rope_event(tc, false, true, smem);
+        rope_event(tc, nullptr, smem);
     f32x16 sacc;
     if (!loader) sacc = scores(smem);
     uint64_t mword_c = mword_n;
@@ -649,10 +627,12 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
+    bool q_copied = false;  // kRope: this iteration's q rows were rotated in this tile's K area
     // Software pipeline: iteration it computes the scores of tile it+1 (MFMA)
     // next to the softmax of tile it (VALU), then PV of tile it.
     for (int it = 0;; ++it) {
         const bool has_next = wn.x < len;
+        q_copied = false;
         Tile tn;
         bool from0_n = from0_c;
         if (has_next) {
@@ -661,20 +641,35 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             barrier_lds();
             if (wf.x < len) fetch();
             tn = plan::peek(wn, len);
+            // kRope: the q rows at a segment start are rotated in the Q slot, or in a copy
+            // in this tile's K area (dead since its scores), with the tree rows of the
+            // tile just landed (a new sequence's positions landed with an earlier tile)
+            unsigned char* q_rot = nullptr;
+            unsigned char* const q_copy = smem + (it % kStages) * kStageBytes;
             if (tn.seg_start) {
                 if (q_slot_tile == it + 1) {
-                    if (!loader) read_q_slot();
+                    if (kRope) q_rot = qslot;
+                    else if (!loader) read_q_slot();
                     q_slot_tile = -1;  // free once every wave has passed the next barrier
-                } else if (!loader) {
-                    load_q_direct(tn);  // rare (short segments)
+                } else {
+                    if (!loader) load_q_direct(tn);  // rare (short segments)
+                    if (kRope) {
+                        if (!loader) write_q_rows(q_copy);
+                        q_rot = q_copy;
+                        barrier_lds();
+                    }
                 }
                 from0_n = tn.key0 == 0;
             }
-            // q rows at a segment start, the tree rows of the tile just landed (a new
-            // sequence's positions landed with an earlier tile)
             const bool k_tree = kRope && tn.key0 + tn.nkeys > tn.S - T;
-            if (kRope && (tn.seg_start || k_tree))
-                rope_event(tn, tn.seg_start, k_tree, smem + ((it + 1) % kStages) * kStageBytes);
+            if (kRope && (q_rot || k_tree)) {
+                rope_event(tn, q_rot, k_tree ? smem + ((it + 1) % kStages) * kStageBytes : nullptr);
+                if (!loader && q_rot) {
+                    if (q_rot == qslot) read_q_slot();
+                    else read_q_rows(q_copy);
+                }
+                q_copied = q_rot == q_copy;
+            }
         }
 
         f32x16 snext;
@@ -774,7 +769,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             // the next stage barrier. ----
             // Without a next tile no stage barrier has passed since the scores of
             // this tile were read from K: wait for every wave before overwriting it.
-            if (!has_next) barrier_lds();
+            if (!has_next || q_copied) barrier_lds();  // q_copied: the q copy there was just read
             unsigned char* const stg = smem + (it % kStages) * kStageBytes;
             f16x4* const xch = reinterpret_cast<f16x4*>(stg);  // [2 sender ks][2 rb][2 db&1][4 qd][64 lanes]
             unsigned char* const obuf = stg + kTileBytes;       // [64 rows][16 chunks of 16 B], swizzled
