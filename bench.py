@@ -478,6 +478,11 @@ def main():
         metric = f"tree-verify steps/sec + tree-attn HBM GB/s (% peak), {w.name}"
     kernel = ("tree_attn_bf16_kernel + tree_attn_merge_kernel (one eagle_tree_attention call)" if w.dtype == "bf16"
               else "tree_attn_f32_kernel (one eagle_tree_attention call)")
+    if w.ctx_range is not None:
+        ctx_label = f"ctx {w.ctx_range[0]}-{w.ctx_range[1]} (ragged, packed cache)"
+        ctx_field = [int(x) for x in vs.ctx_lens_np]
+    else:
+        ctx_label, ctx_field = f"ctx {w.ctx}", w.ctx
     out = {
         "metric": metric,
         "value": round(1000.0 / ms_step, 2),
@@ -492,10 +497,10 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: draft tree d{w.depth} k{w.topk} m{w.m} n{w.n} (T={w.T}), vocab {w.vocab}, "
-                        f"tree attention {w.layers} layers x {w.n_q_heads}q/{w.n_kv_heads}kv heads x {w.head_dim}, "
-                        f"{w.dtype} KV at ctx {w.ctx}, verify temperature {temperature}",
-            "batch": w.batch, "ctx_len": w.ctx, "tree_rows": w.T, "layers": w.layers,
+            "workload": f"{w.name}: {w.batch} x draft tree d{w.depth} k{w.topk} m{w.m} n{w.n} (T={w.T}), "
+                        f"vocab {w.vocab}, tree attention {w.layers} layers x {w.n_q_heads}q/{w.n_kv_heads}kv heads "
+                        f"x {w.head_dim}, {w.dtype} KV at {ctx_label}, verify temperature {temperature}",
+            "batch": w.batch, "ctx_len": ctx_field, "tree_rows": w.T, "layers": w.layers,
             "graph": bool(args.graph), "parallelism": "single GPU",
             "attention_input_copies": rot,
         },

@@ -224,7 +224,7 @@ int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* positi
  * current device).  Nothing in it needs clearing between calls.  The call
  * allocates and frees nothing.  A shape whose eagle_tree_attention_workspace
  * exceeded EAGLE_NOALLOC_SCRATCH_BYTES would get EAGLE_ERR_WORKSPACE (nothing
- * launched; the BF16 workspace is about 4.5 MB for every shape, so none does);
+ * launched; the BF16 workspace is 8,650,752 bytes for every shape, so none does);
  * other checks as eagle_tree_attention.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (other streams, other threads) race; order them on one stream. */
