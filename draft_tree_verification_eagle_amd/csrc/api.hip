@@ -122,10 +122,11 @@ static int attn_desc_check(const eagle_attn_desc* d) {
         return EAGLE_ERR_INVALID_ARG;
     if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return EAGLE_ERR_INVALID_ARG;
     if (d->T > EAGLE_MAX_TREE_ROWS) return EAGLE_ERR_UNSUPPORTED;
-    if (d->dtype == EAGLE_BF16 &&
-        (d->head_dim != 128 || d->batch > attention_max_batch() || !eagle::attention_split_fits(*d)))
+    if (d->head_dim > 128) return EAGLE_ERR_UNSUPPORTED;
+    if (d->dtype == EAGLE_BF16 && d->head_dim == 128 &&
+        (d->batch > attention_max_batch() || !eagle::attention_split_fits(*d)))
         return EAGLE_ERR_UNSUPPORTED;
-    if (d->dtype == EAGLE_F32 && d->head_dim > 128) return EAGLE_ERR_UNSUPPORTED;
+    if (d->batch > EAGLE_MAX_BATCH) return EAGLE_ERR_UNSUPPORTED;
     if ((d->ctx_len_host == nullptr) != (d->kv_row_off_host == nullptr)) return EAGLE_ERR_INVALID_ARG;
     if (d->ctx_len_host) {
         for (int b = 0; b < d->batch; ++b) {
@@ -159,7 +160,7 @@ int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* positi
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const int st = attn_desc_check(desc);
     if (st != EAGLE_OK) return st;
-    if (desc->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
+    if (desc->dtype != EAGLE_BF16 || desc->head_dim != 128) return EAGLE_ERR_UNSUPPORTED;
     if (!(base > 0.0) || isinf(base)) return EAGLE_ERR_INVALID_ARG;
     if (desc->batch == 0) return EAGLE_OK;
     if (!position || !q || !k_cache || !v_cache || !mask || !o || !desc->ctx_len || !desc->kv_row_off)

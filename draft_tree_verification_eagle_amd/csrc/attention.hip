@@ -1183,12 +1183,13 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
 // ---------------------------------------------------------------------------
 // FP32 path: one wave per (tree row, query head).
 // ---------------------------------------------------------------------------
+template <class E>
 struct AttnF32Args {
-    const float* q;
-    const float* k;
-    const float* v;
+    const E* q;
+    const E* k;
+    const E* v;
     const uint64_t* mask;
-    float* o;
+    E* o;
     float* lse;
     const int32_t* ctx_len;
     const int64_t* kv_row_off;
@@ -1197,7 +1198,16 @@ struct AttnF32Args {
     float scale;
 };
 
-// One workgroup of four waves per (tree row, query head).  Keys in blocks of 64,
+// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16) widened to fp32.
+__device__ __forceinline__ float4 load4_f32(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4_f32(const __bf16* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+// Any head_dim up to 128, fp32 or bf16 storage (fp32 arithmetic; a bf16 output is
+// rounded once, to nearest even).  One workgroup of four waves per (tree row, query head).  Keys in blocks of 64,
 // dealt to the waves in turn (block j to wave j mod 4), each wave running an online
 // softmax over its blocks: lane c scores key k0 + c in full (q broadcast from LDS),
 // one wave maximum and sum per block, then P V with lane = head dimension (two per
@@ -1206,7 +1216,8 @@ struct AttnF32Args {
 // (max, sum, output) are combined through LDS.
 constexpr int kF32Waves = 4;
 
-__global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Args a) {
+template <class E>
+__global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Args<E> a) {
     __shared__ __attribute__((aligned(16))) float s_q[128];
     __shared__ float s_ml[2][kF32Waves];
     __shared__ float s_o[kF32Waves][128];
@@ -1215,8 +1226,8 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
     const int g = hq / a.G;
     const int ctx = a.ctx_len[b], S = ctx + a.T, D = a.D;
     const uint64_t mword = a.mask[(int64_t)b * a.T + i];
-    const float* qrow = a.q + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
-    if (threadIdx.x < D) s_q[threadIdx.x] = qrow[threadIdx.x] * a.scale;
+    const E* qrow = a.q + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
+    if (threadIdx.x < D) s_q[threadIdx.x] = (float)qrow[threadIdx.x] * a.scale;
     __syncthreads();
     const int64_t base = ((int64_t)g * a.kv_rows_total + a.kv_row_off[b]) * D;
     float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
@@ -1225,15 +1236,14 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
         const bool vis = c < S && (c < ctx || ((mword >> (c - ctx)) & 1ull));
         float s = -INFINITY;
         if (vis) {
-            const float* kr = a.k + base + (int64_t)c * D;
+            const E* kr = a.k + base + (int64_t)c * D;
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if ((D & 3) == 0) {  // rows are 16-byte aligned: vector loads, eight in flight
+            if ((D & 3) == 0) {  // rows aligned for 4-element loads: vector loads, eight in flight
                 for (int d0 = 0; d0 < D; d0 += 32) {
                     float4 kv[8];
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
-                        kv[u] = d0 + 4 * u < D ? *reinterpret_cast<const float4*>(kr + d0 + 4 * u)
-                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        kv[u] = d0 + 4 * u < D ? load4_f32(kr + d0 + 4 * u) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         if (d0 + 4 * u < D) {
@@ -1246,7 +1256,7 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
                     }
                 }
             } else {
-                for (int d = 0; d < D; ++d) acc[d & 3] += s_q[d] * kr[d];
+                for (int d = 0; d < D; ++d) acc[d & 3] += s_q[d] * (float)kr[d];
             }
             s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         }
@@ -1261,14 +1271,14 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
         m = m_new;
         // P V: the V rows of 16 keys requested together; invisible keys have p = 0
         const int nk = S - k0 < kWave ? S - k0 : kWave;
-        const float* vb = a.v + base + (int64_t)k0 * D;
+        const E* vb = a.v + base + (int64_t)k0 * D;
         for (int j0 = 0; j0 < nk; j0 += 16) {
             float v0[16], v1[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const bool ok = j0 + u < nk;
-                v0[u] = ok && lane < D ? vb[(int64_t)(j0 + u) * D + lane] : 0.0f;
-                v1[u] = ok && lane + kWave < D ? vb[(int64_t)(j0 + u) * D + lane + kWave] : 0.0f;
+                v0[u] = ok && lane < D ? (float)vb[(int64_t)(j0 + u) * D + lane] : 0.0f;
+                v1[u] = ok && lane + kWave < D ? (float)vb[(int64_t)(j0 + u) * D + lane + kWave] : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -1298,9 +1308,9 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
         if (lane < D) r0 += s_o[w][lane] * sc;
         if (lane + kWave < D) r1 += s_o[w][lane + kWave] * sc;
     }
-    float* orow = a.o + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
-    if (lane < D) orow[lane] = r0 / L;
-    if (lane + kWave < D) orow[lane + kWave] = r1 / L;
+    E* orow = a.o + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
+    if (lane < D) orow[lane] = (E)(r0 / L);
+    if (lane + kWave < D) orow[lane + kWave] = (E)(r1 / L);
     if (lane == 0 && a.lse) a.lse[((int64_t)b * a.T + i) * a.Hq + hq] = M + logf(L);
 }
 
@@ -1313,7 +1323,7 @@ struct WsLayout {
 // Partial slots of one launch (reused, in stream order, by the next launch).
 WsLayout ws_layout(const eagle_attn_desc& d) {
     WsLayout w{0, 0, 0};
-    if (d.dtype != EAGLE_BF16) return w;
+    if (d.dtype != EAGLE_BF16 || d.head_dim != kD) return w;
     const size_t slots = 2 * (size_t)kGridWG;
     w.part_o = 0;
     w.part_ml = align_up(slots * kUnitRows * kD * sizeof(_Float16));
@@ -1365,7 +1375,7 @@ int host_plan(HostPlan& hp, MergePlan& mp, const int32_t* ctx, const int64_t* ro
 size_t attention_workspace_bytes(const eagle_attn_desc& d) { return ws_layout(d).total; }
 
 bool attention_split_fits(const eagle_attn_desc& d) {
-    if (d.dtype != EAGLE_BF16) return true;
+    if (d.dtype != EAGLE_BF16 || d.head_dim != kD) return true;
     // the cost line of one launch, bounded through sum_b ceil(S_b / 64) <=
     // ceil(kv_rows_total / 64) + B (the sequences' rows lie inside the cache)
     const int64_t G = d.n_q_heads / d.n_kv_heads;
@@ -1381,13 +1391,18 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
     const bool rope = rope_position != nullptr;
     const float scale = d.scale != 0.0f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
     const int G = d.n_q_heads / d.n_kv_heads;
-    if (d.dtype == EAGLE_F32) {
-        AttnF32Args a;
-        a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
-        a.mask = mask; a.o = (float*)o; a.lse = lse;
-        a.ctx_len = d.ctx_len; a.kv_row_off = d.kv_row_off; a.kv_rows_total = d.kv_rows_total;
-        a.T = d.T; a.Hq = d.n_q_heads; a.G = G; a.D = d.head_dim; a.scale = scale;
-        tree_attn_f32_kernel<<<dim3(d.T, d.n_q_heads, d.batch), kF32Waves * 64, 0, stream>>>(a);
+    if (d.dtype == EAGLE_F32 || d.head_dim != kD) {  // any head_dim <= 128: the row-per-workgroup kernel
+        auto run = [&](auto tag) {
+            using E = decltype(tag);
+            AttnF32Args<E> a;
+            a.q = (const E*)q; a.k = (const E*)k; a.v = (const E*)v;
+            a.mask = mask; a.o = (E*)o; a.lse = lse;
+            a.ctx_len = d.ctx_len; a.kv_row_off = d.kv_row_off; a.kv_rows_total = d.kv_rows_total;
+            a.T = d.T; a.Hq = d.n_q_heads; a.G = G; a.D = d.head_dim; a.scale = scale;
+            tree_attn_f32_kernel<E><<<dim3(d.T, d.n_q_heads, d.batch), kF32Waves * 64, 0, stream>>>(a);
+        };
+        if (d.dtype == EAGLE_F32) run(float{});
+        else run(__bf16{});
         return hipGetLastError();
     }
     const WsLayout w = ws_layout(d);

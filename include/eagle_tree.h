@@ -159,16 +159,18 @@ int eagle_tree_mask(const eagle_tree_cfg* cfg, const eagle_tree_state* state,
  * output rounded to nearest even.  F32: fp32 throughout.
  * kv_rows_total must be at least sum_b (ctx_len[b] + T) (not checkable on the
  * host; the call checks kv_rows_total >= batch * T).
- * Supported: BF16 with head_dim 128; F32 with head_dim <= 128; T <= 64;
- * batch <= EAGLE_MAX_BATCH; for BF16 also, with B = min(batch, 256),
+ * Supported: BF16 or F32 with head_dim <= 128; T <= 64; batch <= EAGLE_MAX_BATCH;
+ * for BF16 with head_dim 128 also, with B = min(batch, 256),
  *     n_kv_heads * ceil(G * T / 64) * (4 * (ceil(kv_rows_total / 64) + B) + 16 * B) < 2^31,
- * G = n_q_heads / n_kv_heads (otherwise EAGLE_ERR_UNSUPPORTED).  BF16 runs one
- * main kernel launch per 256 sequences -- the (sequence, KV head, row group)
- * units of all of them are split over the GPU's compute units together -- and one
- * merge launch for the units split between workgroups (none when no unit is).
- * The workspace (eagle_tree_attention_workspace bytes, the same for every BF16
- * shape; none for F32) holds the split-KV partials; it needs no initialisation,
- * and calls that share one must be ordered on one stream.
+ * G = n_q_heads / n_kv_heads (otherwise EAGLE_ERR_UNSUPPORTED).  BF16 with head_dim
+ * 128 runs the streaming MFMA kernels: one main kernel launch per 256 sequences --
+ * the (sequence, KV head, row group) units of all of them are split over the GPU's
+ * compute units together -- and one merge launch for the units split between
+ * workgroups (none when no unit is).  Other head sizes, and F32, run one workgroup
+ * per (tree row, query head) in fp32 arithmetic (a BF16 output rounded once to
+ * nearest even).  The workspace (eagle_tree_attention_workspace bytes: 8,650,752
+ * for BF16 with head_dim 128, none otherwise) holds the split-KV partials; it needs
+ * no initialisation, and calls that share one must be ordered on one stream.
  * ctx_len_host / kv_row_off_host: optional host copies of ctx_len and kv_row_off
  * (both or neither; NULL = the kernels read the device arrays).  When given they
  * must hold the same values as the device arrays, and the BF16 kernels take each
@@ -207,7 +209,8 @@ int eagle_tree_attention(const eagle_attn_desc* desc, const void* q, const void*
  * eagle_tree_rope followed by eagle_tree_attention within the bf16 tolerance, not
  * bit for bit.  Afterwards the tree rows' K in k_cache are rotated exactly as
  * eagle_tree_rope(q = NULL) leaves them (so eagle_kv_commit applies unchanged);
- * q is not modified, V is not touched.  BF16 only (F32 is EAGLE_ERR_UNSUPPORTED);
+ * q is not modified, V is not touched.  BF16 with head_dim 128 only (any other
+ * shape is EAGLE_ERR_UNSUPPORTED: call eagle_tree_rope, then eagle_tree_attention);
  * base > 0 and finite; other arguments, limits and the workspace as
  * eagle_tree_attention. */
 int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* position, double base, const void* q,
@@ -224,7 +227,7 @@ int eagle_tree_attention_rope(const eagle_attn_desc* desc, const int32_t* positi
  * current device).  Nothing in it needs clearing between calls.  The call
  * allocates and frees nothing.  A shape whose eagle_tree_attention_workspace
  * exceeded EAGLE_NOALLOC_SCRATCH_BYTES would get EAGLE_ERR_WORKSPACE (nothing
- * launched; the BF16 workspace is 8,650,752 bytes for every shape, so none does);
+ * launched; the workspace is at most 8,650,752 bytes for every shape, so none does);
  * other checks as eagle_tree_attention.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (other streams, other threads) race; order them on one stream. */

@@ -148,7 +148,10 @@ def test_attention_validation(eb):
     assert call(_desc(eb, n_kv_heads=3)) == eb.EAGLE_ERR_INVALID_ARG        # 40 % 3 != 0
     assert call(_desc(eb, T=65)) == eb.EAGLE_ERR_UNSUPPORTED
     assert call(_desc(eb, T=0)) == eb.EAGLE_ERR_INVALID_ARG
-    assert call(_desc(eb, head_dim=64)) == eb.EAGLE_ERR_UNSUPPORTED         # bf16 needs 128
+    assert call(_desc(eb, head_dim=130)) == eb.EAGLE_ERR_UNSUPPORTED        # head_dim <= 128
+    # other bf16 head sizes run the row-per-workgroup kernel, which needs no workspace
+    assert L.eagle_tree_attention_workspace(C.byref(_desc(eb, head_dim=64))) == 0
+    assert L.eagle_tree_attention_workspace(C.byref(_desc(eb, head_dim=96))) == 0
     assert call(_desc(eb, dtype=7)) == eb.EAGLE_ERR_INVALID_ARG
     assert call(_desc(eb, scale=-1.0)) == eb.EAGLE_ERR_INVALID_ARG
     assert call(_desc(eb, scale=float("nan"))) == eb.EAGLE_ERR_INVALID_ARG
@@ -352,7 +355,7 @@ def test_noalloc_attention_validation(eb):
     assert 0 < eb.eagle_tree_attention_workspace(d) <= (16 << 20)
     d2 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 128, Dev(), Dev(), 4096)
     assert L.eagle_tree_attention_noalloc(C.byref(d2), None, f, f, f, f, None, None) == eb.EAGLE_ERR_INVALID_ARG
-    d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 96, Dev(), Dev(), 4096)
+    d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 130, Dev(), Dev(), 4096)
     assert L.eagle_tree_attention_noalloc(C.byref(d3), f, f, f, f, f, None, None) == eb.EAGLE_ERR_UNSUPPORTED
     d4 = eb.make_attn_desc(eb.EAGLE_BF16, 0, 16, 8, 8, 128, Dev(), Dev(), 4096)
     assert L.eagle_tree_attention_noalloc(C.byref(d4), f, f, f, f, f, None, None) == eb.EAGLE_OK  # empty batch

@@ -385,6 +385,11 @@ EDGE = [
     dict(depth=4, topk=32, m=32, n=63, vocab=262144, batch=2, ctx=100, seed=13),  # largest vocabulary, top-k
                                                            # and T; 3105 of the 4096 node slots
     dict(batch=1024, ctx_range=(0, 60), n=8, seed=17),     # largest batch
+    # bf16 head sizes other than 128 (the row-per-workgroup kernel): vector loads, and
+    # a size that is not a multiple of 4 (element loads)
+    dict(head_dim=64, n_q_heads=8, n_kv_heads=2, ctx=300, n=12, seed=19),
+    dict(head_dim=96, batch=3, ctx_range=(0, 500), n=14, seed=23),
+    dict(head_dim=34, ctx=70, n=10, seed=29),
 ]
 
 
