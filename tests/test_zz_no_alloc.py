@@ -78,5 +78,5 @@ def test_noalloc_size_limit_and_bad_arguments(lib):
     assert 0 < eb.eagle_tree_attention_workspace(d) <= (16 << 20)
     d2 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 128, dev, dev, 4096)
     assert L.eagle_tree_attention_noalloc(C.byref(d2), None, f, f, f, f, None, None) == eb.EAGLE_ERR_INVALID_ARG
-    d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 96, dev, dev, 4096)
+    d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 130, dev, dev, 4096)  # head_dim > 128: rejected
     assert L.eagle_tree_attention_noalloc(C.byref(d3), f, f, f, f, f, None, None) == eb.EAGLE_ERR_UNSUPPORTED
