@@ -203,6 +203,7 @@ struct HostPlan {
     int64_t row0[kArgSeqs];
     uint32_t cost0[kArgSeqs + 1];
     int64_t key0[kArgSeqs + 1];
+    plan::Recip rW[kArgSeqs];  // division by the sequence's unit cost
 };
 
 struct AttnArgs {
@@ -221,6 +222,9 @@ struct AttnArgs {
     float scale_log2;
     int32_t one_S;             // kOne: the one sequence's keys (ctx + T) and first row
     int64_t one_row0;
+    plan::Recip one_rW;        // kOne: division by the sequence's unit cost
+    plan::Split sp_h;          // kOne, kHostTab: the work split, with the reciprocal of its stretch count
+    plan::Recip rRG, rT;       // division by RG and by T
     const int32_t* rope_pos;   // kRope: tree rows' positions [B][T]
     double rope_turns[kD / 2]; // kRope: base^(-2d/D) / (2 pi), turns per position
     HostPlan hp;               // kHostTab only
@@ -234,16 +238,19 @@ struct ArgTab {
     __host__ __device__ int64_t row0(int b) const { return hp->row0[b]; }
     __host__ __device__ uint32_t cost0(int b) const { return hp->cost0[b]; }
     __host__ __device__ int64_t key0(int b) const { return hp->key0[b]; }
+    __host__ __device__ uint32_t unit_of(int b, uint32_t c) const { return plan::div_by(c, hp->rW[b]); }
 };
 // One sequence whose length the host knows: every entry from two scalar arguments.
 struct OneTab {
     int32_t S0;
     int64_t r0;
     int UPS;
+    plan::Recip rW;
     __device__ int S(int) const { return S0; }
     __device__ int64_t row0(int) const { return r0; }
     __device__ uint32_t cost0(int b) const { return b == 0 ? 0u : (uint32_t)UPS * plan::unit_cost(S0); }
     __device__ int64_t key0(int b) const { return b == 0 ? 0 : (int64_t)UPS * S0; }
+    __device__ uint32_t unit_of(int, uint32_t c) const { return plan::div_by(c, rW); }
 };
 struct LdsTab {
     const int32_t* s;
@@ -254,12 +261,13 @@ struct LdsTab {
     __device__ int64_t row0(int b) const { return r[b]; }
     __device__ uint32_t cost0(int b) const { return c[b]; }
     __device__ int64_t key0(int b) const { return k[b]; }
+    __device__ uint32_t unit_of(int b, uint32_t c) const { return c / plan::unit_cost(s[b]); }
 };
 
 // Packed query row -> (tree row, query head); rows past G*T map to row 0.
 __device__ __forceinline__ void query_row(const AttnArgs& a, int g, int rp, int& i, int& hq) {
     if (rp >= a.G * a.T) rp = 0;
-    const int gi = rp / a.T;
+    const int gi = (int)plan::div_by((uint32_t)rp, a.rT);
     i = rp - gi * a.T;
     hq = g * a.G + gi;
 }
@@ -414,7 +422,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
 
     const int T = a.T;
     const int B = a.B, UPS = a.Hkv * a.RG;
-    Walker w0 = plan::walker_at(tab, a.RG, tb);
+    Walker w0 = plan::walker_at(tab, a.RG, a.rRG, tb);
 
     // ---- first segment's Q and mask word, straight into registers ----
     const int qrow = 32 * rb + l32;  // this lane's packed query row inside the unit
@@ -983,8 +991,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
             tile_loop<false, kRope>(a, tab, smem, qslot, mslot, s_ml, rl, wid, lane, vwg, len, tb);
     };
     if constexpr (kMode == kOne) {
-        const OneTab tab{a.one_S, a.one_row0, UPS};
-        const Split sp = plan::make_split(tab.cost0(1), (int)gridDim.x, UPS);
+        const OneTab tab{a.one_S, a.one_row0, UPS, a.one_rW};
+        const Split sp = a.sp_h;  // make_split(cost0(1), gridDim.x, UPS), from the host
         const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
         if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
         const Pos tb = plan::split_tile(tab, 1, UPS, plan::stretch_start(sp, vwg));
@@ -994,7 +1002,7 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
         walk(tab, vwg, (int)(x_end - x_begin), tb);
     } else if constexpr (kMode == kHostTab) {
         const ArgTab tab{&a.hp};
-        const Split sp = plan::make_split(a.hp.cost0[B], (int)gridDim.x, B * UPS);
+        const Split sp = a.sp_h;  // make_split(cost0[B], gridDim.x, B * UPS), from the host
         const int vwg = xcd_first(xcd, sp.nwg) + (blockIdx.x >> 3);
         if (vwg >= xcd_first(xcd + 1, sp.nwg)) return;  // nwg <= gridDim.x: every stretch has a workgroup
         const Pos tb = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, vwg));
@@ -1045,6 +1053,7 @@ struct MergeArgs {
     const int32_t* ctx_len;
     const int64_t* kv_row_off;
     int B, T, Hq, Hkv, G, RG;
+    plan::Recip rRG, rT;         // division by RG and by T
     int n_merge;                 // workgroups of the merge proper; kRope: the rest rotate the cache
     // kRope: the tree rows' K in the cache, rotated in place as the rotary call does
     uint16_t* k;
@@ -1064,7 +1073,7 @@ struct MergeArgs {
 template <bool kHostPlan>
 __device__ __forceinline__ void rope_cache_rows(const MergeArgs& m, int x) {
     const int slices = (m.Hkv + 15) / 16;
-    const int i = x % m.T, rest = x / m.T;
+    const int rest = (int)plan::div_by((uint32_t)x, m.rT), i = x - rest * m.T;
     const int slice = rest % slices, b = rest / slices;
     const int d = threadIdx.x & 63, grp = threadIdx.x >> 6;
     const int64_t krow = kHostPlan ? m.krow_h[b] + i : m.kv_row_off[b] + (int64_t)m.ctx_len[b] + i;
@@ -1127,7 +1136,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
         if (!plan::split_unit_from(tab, sp, m.B, UPS, v, te, b, uis, vl)) return;
         vf = v;
     }
-    const int g = uis / m.RG, rg = uis - g * m.RG;
+    const int g = (int)plan::div_by((uint32_t)uis, m.rRG), rg = uis - g * m.RG;
     const int row = rb * 16 + (tid >> 4);
     const int d0 = (tid & 15) * 8;
     const int rp = rg * kUnitRows + row;
@@ -1171,7 +1180,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
         }
         M = Mn;
     }
-    const int gi = rp / m.T, i = rp - gi * m.T, hq = g * m.G + gi;
+    const int gi = (int)plan::div_by((uint32_t)rp, m.rT), i = rp - gi * m.T, hq = g * m.G + gi;
     const float inv = 1.0f / L;
     bf16x8 out;
 #pragma unroll
@@ -1336,17 +1345,19 @@ WsLayout ws_layout(const eagle_attn_desc& d) {
 // on the XCD that computed the unit's middle piece.  Returns the merge workgroups
 // to launch, or -1 when the plan does not fit kPlanWgs (the merge kernel then
 // finds the split units itself).
-int host_plan(HostPlan& hp, MergePlan& mp, const int32_t* ctx, const int64_t* row0, int B, int T, int UPS) {
+int host_plan(HostPlan& hp, MergePlan& mp, Split& sp, const int32_t* ctx, const int64_t* row0, int B, int T,
+              int UPS) {
     hp.cost0[0] = 0;
     hp.key0[0] = 0;
     for (int b = 0; b < B; ++b) {
         hp.S[b] = ctx[b] + T;
         hp.row0[b] = row0[b];
+        hp.rW[b] = plan::recip_of(plan::unit_cost(hp.S[b]));
         hp.cost0[b + 1] = hp.cost0[b] + (uint32_t)UPS * plan::unit_cost(hp.S[b]);
         hp.key0[b + 1] = hp.key0[b] + (int64_t)UPS * hp.S[b];
     }
     const ArgTab tab{&hp};
-    const Split sp = plan::make_split(hp.cost0[B], kGridWG, B * UPS);
+    sp = plan::make_split_recip(hp.cost0[B], kGridWG, B * UPS);
     uint64_t by_xcd[8][kPlanWgs];
     int n_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int v = 0; v < sp.nwg; ++v) {
@@ -1428,6 +1439,8 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         a.part_ml = (uint64_t*)(ws + w.part_ml);
         a.kv_rows_total = d.kv_rows_total;
         a.B = nb; a.T = d.T; a.Hq = d.n_q_heads; a.Hkv = d.n_kv_heads; a.G = G; a.RG = RG;
+        a.rRG = plan::recip_of((uint32_t)RG);
+        a.rT = plan::recip_of((uint32_t)d.T);
         a.scale_log2 = scale * kLog2e;
         a.rope_pos = rope ? rope_position + (size_t)b0 * d.T : nullptr;
         MergeArgs m;
@@ -1438,6 +1451,8 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         m.ctx_len = a.ctx_len;
         m.kv_row_off = a.kv_row_off;
         m.B = nb; m.T = d.T; m.Hq = d.n_q_heads; m.Hkv = d.n_kv_heads; m.G = G; m.RG = RG;
+        m.rRG = a.rRG;
+        m.rT = a.rT;
         m.k = (uint16_t*)k;
         m.kv_rows_total = d.kv_rows_total;
         m.rope_pos = a.rope_pos;
@@ -1454,9 +1469,11 @@ hipError_t launch_attention(const eagle_attn_desc& d, const void* q, const void*
         const bool host = d.ctx_len_host && nb <= kArgSeqs && UPS < (1 << 24);
         hipError_t e;
         if (host) {
-            const int merge_wg = host_plan(a.hp, m.mp, d.ctx_len_host + b0, d.kv_row_off_host + b0, nb, d.T, UPS);
+            const int merge_wg =
+                host_plan(a.hp, m.mp, a.sp_h, d.ctx_len_host + b0, d.kv_row_off_host + b0, nb, d.T, UPS);
             a.one_S = a.hp.S[0];
             a.one_row0 = a.hp.row0[0];
+            a.one_rW = a.hp.rW[0];
             for (int b = 0; b < nb; ++b) m.krow_h[b] = a.hp.row0[b] + (a.hp.S[b] - d.T);
             // 4 computing waves + 4 loaders per workgroup
             if (nb == 1 && rope)

@@ -29,7 +29,9 @@
 // holds while the next stretch starts inside it.
 //
 // Tables.  The functions take the per-sequence table as an object with
-// S(b) (keys), row0(b) (first cache row), cost0(b) and key0(b) (prefixes, b <= B).
+// S(b) (keys), row0(b) (first cache row), cost0(b) and key0(b) (prefixes, b <= B),
+// and unit_of(b, c) = c / unit_cost(S(b)) (a table built from host lengths holds
+// each sequence's reciprocal of that cost).
 #pragma once
 
 #include <stdint.h>
@@ -47,6 +49,24 @@ constexpr uint32_t kSegCost = 16;
 constexpr int kMaxSeqs = 256;  // sequences per launch (the per-sequence table lives in LDS)
 constexpr int kMaxPieces = 32;  // stretches per unit on average, at most
 
+// Division by a divisor fixed for a launch, as a multiply and a shift: with
+// l = ceil(log2 d) and m = ceil(2^(31 + l) / d), floor(n / d) = floor(n m / 2^(31 + l))
+// for every 0 <= n < 2^31 (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994: m d = 2^(31+l) + e with 0 <= e < d <= 2^l, so the
+// product overshoots n / d by n e / (d 2^(31+l)) < 1 / d, which never reaches the
+// next integer).  The host computes (m, 31 + l); m <= 2^32, so n m < 2^63.
+struct Recip {
+    uint64_t m;
+    uint32_t sh;
+};
+inline Recip recip_of(uint32_t d) {  // 1 <= d < 2^31
+    uint32_t l = 0;
+    while ((1u << l) < d) ++l;
+    const uint64_t p = 1ull << (31 + l);
+    return Recip{(p + d - 1) / d, 31 + l};
+}
+EAGLE_HD inline uint32_t div_by(uint32_t n, const Recip& r) { return (uint32_t)(((uint64_t)n * r.m) >> r.sh); }
+
 EAGLE_HD inline int tiles_of(int S) { return (S + kTileKeys - 1) / kTileKeys; }
 EAGLE_HD inline uint32_t unit_cost(int S) { return 4u * (uint32_t)tiles_of(S) + kSegCost; }
 
@@ -54,6 +74,7 @@ struct Split {
     uint32_t Wt;    // cost steps in all
     uint32_t q, r;  // Wt = q * nwg + r
     int nwg;        // stretches (workgroups that take part)
+    Recip rn;       // division by nwg; m == 0: not computed (plain division)
 };
 EAGLE_HD inline Split make_split(uint32_t Wt, int grid, int units) {
     Split sp;
@@ -63,11 +84,19 @@ EAGLE_HD inline Split make_split(uint32_t Wt, int grid, int units) {
     sp.nwg = most < (uint32_t)grid ? (most > 0 ? (int)most : 1) : grid;
     sp.q = Wt / (uint32_t)sp.nwg;
     sp.r = Wt - sp.q * (uint32_t)sp.nwg;
+    sp.rn = Recip{0, 0};
+    return sp;
+}
+// The same with the reciprocal of nwg (host side).
+inline Split make_split_recip(uint32_t Wt, int grid, int units) {
+    Split sp = make_split(Wt, grid, units);
+    sp.rn = recip_of((uint32_t)sp.nwg);
     return sp;
 }
 // First cost step of stretch v (v = nwg gives Wt): floor(Wt * v / nwg).
 EAGLE_HD inline uint32_t stretch_start(const Split& sp, int v) {
-    return sp.q * (uint32_t)v + (sp.r * (uint32_t)v) / (uint32_t)sp.nwg;
+    const uint32_t rv = sp.r * (uint32_t)v;  // < nwg * (nwg + 1)
+    return sp.q * (uint32_t)v + (sp.rn.m ? div_by(rv, sp.rn) : rv / (uint32_t)sp.nwg);
 }
 // The stretch holding cost step p < Wt.
 EAGLE_HD inline int stretch_of(const Split& sp, uint32_t p) {
@@ -108,7 +137,7 @@ EAGLE_HD inline Pos split_tile(const Tab& tab, int B, int UPS, uint32_t p) {
     const int S = tab.S(t.b);
     const uint32_t W = unit_cost(S);
     const uint32_t local = p - tab.cost0(t.b);
-    t.uis = (int)(local / W);
+    t.uis = (int)tab.unit_of(t.b, local);
     const uint32_t r = local - (uint32_t)t.uis * W;
     t.tile = r <= kSegCost ? 0 : (int)((r - kSegCost + 3) / 4);
     if (t.tile >= tiles_of(S)) {
@@ -149,13 +178,14 @@ struct Tile {
     int64_t row0;
     bool seg_start, seg_end;
 };
+// rRG: division by RG (the host computes it for every launch).
 template <class Tab>
-EAGLE_HD inline Walker walker_at(const Tab& tab, int RG, const Pos& t) {
+EAGLE_HD inline Walker walker_at(const Tab& tab, int RG, const Recip& rRG, const Pos& t) {
     Walker w;
     w.x = 0;
     w.b = t.b;
     w.uis = t.uis;
-    w.g = t.uis / RG;
+    w.g = (int)div_by((uint32_t)t.uis, rRG);
     w.rg = t.uis - w.g * RG;
     w.key0 = t.tile * kTileKeys;
     w.S = tab.S(t.b);

@@ -15,7 +15,9 @@
 //   * stretch_of maps each tile's cost step to the workgroup that takes it;
 //   * a stretch holds at most two pieces: its first segment (not from0) and its
 //     last (from0);
-//   * the workgroup -> stretch map (XCD runs) gives each stretch one workgroup.
+//   * the workgroup -> stretch map (XCD runs) gives each stretch one workgroup;
+//   * every division the kernel takes from a host reciprocal (by the stretch count,
+//     by a sequence's unit cost, by RG and by T) equals the plain division.
 // Input (stdin): grid T Hq Hkv rows_total B, then B pairs (ctx, row0).
 #define EAGLE_HD
 #include "../../draft_tree_verification_eagle_amd/csrc/attn_plan.hpp"
@@ -29,19 +31,6 @@
 
 using namespace eagle::plan;
 
-struct HostTab {
-    const int32_t* S_;
-    const int64_t* row0_;
-    const uint32_t* cost0_;
-    const int64_t* key0_;
-    int S(int b) const { return S_[b]; }
-    int64_t row0(int b) const { return row0_[b]; }
-    uint32_t cost0(int b) const { return cost0_[b]; }
-    int64_t key0(int b) const { return key0_[b]; }
-};
-
-static int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
-
 #define CHECK(c)                                                                         \
     do {                                                                                 \
         if (!(c)) {                                                                      \
@@ -49,6 +38,27 @@ static int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
             std::abort();                                                                \
         }                                                                                \
     } while (0)
+
+// The table the kernel reads from its launch arguments: unit_of by the host
+// reciprocal of each sequence's unit cost, checked against the division.
+struct HostTab {
+    const int32_t* S_;
+    const int64_t* row0_;
+    const uint32_t* cost0_;
+    const int64_t* key0_;
+    const Recip* rW_;
+    int S(int b) const { return S_[b]; }
+    int64_t row0(int b) const { return row0_[b]; }
+    uint32_t cost0(int b) const { return cost0_[b]; }
+    int64_t key0(int b) const { return key0_[b]; }
+    uint32_t unit_of(int b, uint32_t c) const {
+        const uint32_t q = div_by(c, rW_[b]);
+        CHECK(q == c / unit_cost(S_[b]));
+        return q;
+    }
+};
+
+static int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
 
 int main() {
     int grid, T, Hq, Hkv, B;
@@ -71,16 +81,26 @@ int main() {
     // the table the kernel builds (prefix sums as in its wave scan)
     std::vector<uint32_t> cost0(B + 1, 0);
     std::vector<int64_t> key0(B + 1, 0);
+    std::vector<Recip> rW(B);
     uint64_t wide = 0;
     for (int b = 0; b < B; ++b) {
+        rW[b] = recip_of(unit_cost(S[b]));
         wide += (uint64_t)UPS * unit_cost(S[b]);
         CHECK(wide < (1ull << 31));
         cost0[b + 1] = cost0[b] + (uint32_t)UPS * unit_cost(S[b]);
         key0[b + 1] = key0[b] + (int64_t)UPS * S[b];
     }
-    const HostTab tab{S.data(), row0.data(), cost0.data(), key0.data()};
-    const Split sp = make_split(cost0[B], grid, B * UPS);
+    const HostTab tab{S.data(), row0.data(), cost0.data(), key0.data(), rW.data()};
+    const Split sp = make_split_recip(cost0[B], grid, B * UPS);
     CHECK(sp.nwg >= 1 && sp.nwg <= grid);
+    {
+        Split plain = sp;
+        plain.rn = Recip{0, 0};
+        for (int v = 0; v <= sp.nwg; ++v) CHECK(stretch_start(sp, v) == stretch_start(plain, v));
+    }
+    const Recip rRG = recip_of((uint32_t)RG), rT = recip_of((uint32_t)T);
+    for (int rp = 0; rp < G * T + kUnitRows; ++rp) CHECK(div_by((uint32_t)rp, rT) == (uint32_t)(rp / T));
+    for (int u = 0; u < UPS + RG; ++u) CHECK(div_by((uint32_t)u, rRG) == (uint32_t)(u / RG));
     // workgroup -> stretch
     std::vector<int> owner(sp.nwg, -1);
     for (int blk = 0; blk < grid; ++blk) {
@@ -108,7 +128,7 @@ int main() {
         CHECK(xe - xb < (1ll << 31));
         const int len = (int)(xe - xb);
         CHECK(tb.b < B);
-        Walker w = walker_at(tab, RG, tb);
+        Walker w = walker_at(tab, RG, rRG, tb);
         bool from0 = false;
         int n_pieces = 0, n_segments = 0;
         while (w.x < len) {

@@ -106,3 +106,16 @@ def test_plan_random_descriptors(checker):
             continue  # the host rejects this shape
         for line in launches(T, Hkv * G, Hkv, c, r, total):
             run(checker, line)
+
+
+def test_host_reciprocals(tmp_path):
+    """The multiply-and-shift divisions the kernels take from host reciprocals
+    (attn_plan.hpp recip_of / div_by) equal the plain division for every dividend
+    below 2^31: all divisors up to 4096, random divisors up to 2^31 - 1, powers of
+    two and their neighbours, and two divisors over every dividend."""
+    exe = str(tmp_path / "recip_check")
+    subprocess.check_call(["g++", "-std=c++17", "-O2", "-o", exe,
+                           os.path.join(ROOT, "tests", "replica", "recip_check.cpp")])
+    p = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.strip() == "ok"
