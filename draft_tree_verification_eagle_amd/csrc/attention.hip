@@ -817,6 +817,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
                 // a row that sees none of this segment's keys has ltot = 0: its partial
                 // is all zeros, and its merge weight is zero
                 const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+                const float c0 = a0 * inv, c1 = w1 * inv;  // weights of this half's and the other's values
                 const int row = opaque(32 * rb + l32);
                 // the other half's values for this wave's 64 columns, all read before
                 // any staging write (the two areas share a stage)
@@ -835,7 +836,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
                         V4 w;
 #pragma unroll
                         for (int x = 0; x < 4; ++x)
-                            w[x] = (acc[4 * qd + x] * a0 + (float)o1[db & 1][qd][x] * w1) * inv;
+                            w[x] = __builtin_fmaf((float)o1[db & 1][qd][x], c1, acc[4 * qd + x] * c0);
                         const int c = (4 * db + qd) ^ (row & 15);
                         *reinterpret_cast<V4*>(obuf + row * kRowBytes + c * 16 + h2 * 8) = w;
                     }
@@ -902,12 +903,14 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
                 }
             }
             // the next segment starts from an empty state
+            if (has_next) {
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-            m_run = -INFINITY;
-            l_run = 0.0f;
+                    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+                m_run = -INFINITY;
+                l_run = 0.0f;
+            }
         }
         if (!has_next) break;
         sacc = snext;
