@@ -318,14 +318,21 @@ __global__ __launch_bounds__(kWalkThreads) void verify_walk_kernel(
     // `rest`) and the tokens whose first carrier among the children is c or later;
     // a child whose token an earlier sibling carried has probability 0.
     if (tid < kWave) {
-        // bit j: no earlier sibling of row j carries row j's token (each row's parent
-        // and token broadcast to the wave in turn)
-        const int my_par = lane < T ? s_par[lane] : -2, my_tok = lane < T ? s_tok[lane] : -1;
-        bool first = lane < T;
-        for (int i = 1; i < T; ++i) {
-            const int pi = __builtin_amdgcn_readlane(my_par, i), ti = __builtin_amdgcn_readlane(my_tok, i);
-            if (i < lane && pi == my_par && ti == my_tok) first = false;
+        // bit j: no earlier sibling of row j carries row j's token.  Each row (but the
+        // root) has the key parent * 2^tb + token; the rows sharing a lane's key are
+        // found bit by bit (for every key bit, the rows that agree with the lane on
+        // it, from one ballot), with no per-row loop.
+        int tb = 0;
+        while ((1 << tb) < V) ++tb;  // token bits (V <= 2^18, parent < 64: 24 bits at most)
+        const bool row_ok = lane >= 1 && lane < T;
+        const uint32_t key = row_ok ? ((uint32_t)s_par[lane] << tb) | (uint32_t)s_tok[lane] : 0u;
+        uint64_t same = __ballot(row_ok);
+        for (int bit = 0; bit < tb + 6; ++bit) {
+            const bool on = (key >> bit) & 1u;
+            const uint64_t with_bit = __ballot(on);
+            same &= on ? with_bit : ~with_bit;
         }
+        const bool first = lane < T && (lane == 0 || (same & ((1ull << lane) - 1ull)) == 0);
         const uint64_t firsts = __ballot(first);
         int cur = 0, len = 0;
         while (true) {

@@ -257,7 +257,8 @@ int eagle_tree_attention_noalloc(const eagle_attn_desc* desc, const void* q, con
  * Outputs: accept_len [batch] (0..depth), accept_path [batch][depth] (flattened
  * rows, -1 padded), out_tokens [batch][depth + 1] (accepted tokens then the bonus,
  * -1 padded).  flat_token / flat_parent from eagle_tree_mask (or the caller's
- * static tree: flat_parent[b][0] = -1, 0 <= flat_parent[b][i] < i otherwise).
+ * static tree: flat_parent[b][0] = -1, 0 <= flat_parent[b][i] < i otherwise;
+ * 0 <= flat_token[b][i] < vocab).
  * Only batch, vocab, depth and n of cfg are read (T = n + 1; topk and m are
  * ignored); n + 1 > EAGLE_MAX_TREE_ROWS, vocab > EAGLE_MAX_VOCAB or depth > 255 is
  * EAGLE_ERR_UNSUPPORTED.  Negative or NaN temperature is EAGLE_ERR_INVALID_ARG.
