@@ -82,7 +82,14 @@ static_assert(kRowBatch <= 32, "one 32-bit window of the child mask per step");
 constexpr int kMaxChunkTokens = 256;  // ceil(EAGLE_MAX_VOCAB / 1024)
 static_assert((EAGLE_MAX_VOCAB + kRowChunks - 1) / kRowChunks <= kMaxChunkTokens, "chunk mask");
 static_assert(kRowSplit == 4, "RowStats keeps four partial rest masses");
+// From this many tree rows in a call (batch x T), one workgroup takes a whole row:
+// it finds the maximum once and then does the four quarters' mass passes one after
+// the other, each exactly as that quarter's workgroup would (same threads, same
+// sums), so the statistics are the same bits; the row is read once for its maximum
+// instead of four times, and there are enough rows to fill the GPU.
+constexpr int kWholeRowsFrom = 256;
 
+template <bool kWhole>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     const float* __restrict__ target, int T, int V, const int32_t* __restrict__ flat_token,
     const int32_t* __restrict__ flat_parent, float temperature, RowStats* __restrict__ stats,
@@ -92,11 +99,13 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     __shared__ int s_nk;
     __shared__ uint64_t s_key[kRowWaves];
     __shared__ double s_red[kRowWaves];
-    // blockIdx.x = 8 * (kRowSplit * (i / 8) + q) + i % 8: the quarters of row i share an XCD
+    // kWhole: blockIdx.x = row i, quarters 0..3 in turn.  Otherwise blockIdx.x =
+    // 8 * (kRowSplit * (i / 8) + q) + i % 8: the quarters of row i share an XCD.
     const int xb = blockIdx.x;
-    const int i = 8 * (xb / (8 * kRowSplit)) + (xb & 7), q = (xb >> 3) % kRowSplit;
+    const int i = kWhole ? xb : 8 * (xb / (8 * kRowSplit)) + (xb & 7);
+    const int q_first = kWhole ? 0 : (xb >> 3) % kRowSplit, q_end = kWhole ? kRowSplit : q_first + 1;
     const int b = blockIdx.y, tid = threadIdx.x;
-    if (i >= T || (q > 0 && !(temperature > 0.0f))) return;  // greedy needs the argmax only
+    if (i >= T || (q_first > 0 && !(temperature > 0.0f))) return;  // greedy needs the argmax only
     const int lane = tid & (kWave - 1), wid = tid / kWave;
     const float* z = target + ((size_t)b * T + i) * (size_t)V;
     if (wid == 0) {
@@ -167,71 +176,73 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
         const double fscale = ldexp(1.0, fixed_shift(V));
         const int ch = (V + kRowChunks - 1) / kRowChunks;
-        const int chunk = q * kWgChunks + (tid >> 1), half = tid & 1;
-        const int c0 = min(V, chunk * ch), c1 = min(V, c0 + ch);
-        // the pair of threads splits the chunk: the first takes the first
-        // ceil(ch / 2) tokens rounded up to a multiple of 4, the second the rest
-        const int hc = (((ch + 1) >> 1) + 3) & ~3;
-        const int s0 = half == 0 ? c0 : min(c1, c0 + hc), s1 = half == 0 ? min(c1, c0 + hc) : c1;
-        uint64_t km[4] = {0, 0, 0, 0};  // bit d: token c0 + d is a child of the row
-        for (int c = 0; c < nk; ++c) {
-            const int d = s_kid_tok[c] - c0;
-            if (d >= 0 && d < c1 - c0) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    if ((d >> 6) == w) km[w] |= 1ull << (d & 63);
-            }
-        }
-        double s = 0.0;
-        uint64_t fm = 0;
-        // 16-byte aligned chunk starts: vector loads
-        const bool cvec = vec && (ch & 3) == 0;
-        for (int a0 = s0; a0 < s1; a0 += kRowBatch) {
-            float zz[kRowBatch];
-            if (cvec) {
-#pragma unroll
-                for (int u = 0; u < kRowBatch; u += 4) {
-                    float4 v4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (a0 + u < s1) v4 = *reinterpret_cast<const float4*>(z + a0 + u);
-                    zz[u] = v4.x; zz[u + 1] = v4.y; zz[u + 2] = v4.z; zz[u + 3] = v4.w;
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < kRowBatch; ++u) zz[u] = a0 + u < s1 ? z[a0 + u] : 0.0f;
-            }
-            // bits o .. o + 31 of the chunk's child mask, which may straddle two words
-            const int o = a0 - c0, wo = o >> 6, sh = o & 63;
-            uint64_t lo = km[0], hi = km[1];
-#pragma unroll
-            for (int w = 1; w < 4; ++w)
-                if (wo == w) {
-                    lo = km[w];
-                    hi = w + 1 < 4 ? km[w + 1] : 0;
-                }
-            const uint32_t kb = (uint32_t)(sh == 0 ? lo : (lo >> sh) | (hi << (64 - sh)));
-#pragma unroll
-            for (int u = 0; u < kRowBatch; ++u) {
-                if (a0 + u < s1) {
-                    const double x = (double)zz[u] - (double)zmax;
-                    const double e = exp_nonpos_f64(unit_temp ? x : x / temp);
-                    fm += fixed_mass(e, fscale);
-                    if (!((kb >> u) & 1u)) s += e;
+        for (int q = q_first; q < q_end; ++q) {
+            const int chunk = q * kWgChunks + (tid >> 1), half = tid & 1;
+            const int c0 = min(V, chunk * ch), c1 = min(V, c0 + ch);
+            // the pair of threads splits the chunk: the first takes the first
+            // ceil(ch / 2) tokens rounded up to a multiple of 4, the second the rest
+            const int hc = (((ch + 1) >> 1) + 3) & ~3;
+            const int s0 = half == 0 ? c0 : min(c1, c0 + hc), s1 = half == 0 ? min(c1, c0 + hc) : c1;
+            uint64_t km[4] = {0, 0, 0, 0};  // bit d: token c0 + d is a child of the row
+            for (int c = 0; c < nk; ++c) {
+                const int d = s_kid_tok[c] - c0;
+                if (d >= 0 && d < c1 - c0) {
+    #pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        if ((d >> 6) == w) km[w] |= 1ull << (d & 63);
                 }
             }
-        }
-        // the pair's integer masses add exactly
-        const uint32_t flo = __shfl_xor((uint32_t)fm, 1, kWave), fhi = __shfl_xor((uint32_t)(fm >> 32), 1, kWave);
-        fm += ((uint64_t)fhi << 32) | flo;
-        if (half == 0) chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
-        s = block_sum_f64(s, s_red);
-        if (tid == 0) out->rest[q] = s;
-        // the same expression as the chunk masses' (x / 1 == x exactly), so the bonus
-        // draw can take a removed token's fixed-point mass out of its chunk exactly
-        if (q == 0 && tid < nk)
-            stats[(size_t)b * T + s_kid_row[tid]].e_kid =
-                exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
+            double s = 0.0;
+            uint64_t fm = 0;
+            // 16-byte aligned chunk starts: vector loads
+            const bool cvec = vec && (ch & 3) == 0;
+            for (int a0 = s0; a0 < s1; a0 += kRowBatch) {
+                float zz[kRowBatch];
+                if (cvec) {
+    #pragma unroll
+                    for (int u = 0; u < kRowBatch; u += 4) {
+                        float4 v4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        if (a0 + u < s1) v4 = *reinterpret_cast<const float4*>(z + a0 + u);
+                        zz[u] = v4.x; zz[u + 1] = v4.y; zz[u + 2] = v4.z; zz[u + 3] = v4.w;
+                    }
+                } else {
+    #pragma unroll
+                    for (int u = 0; u < kRowBatch; ++u) zz[u] = a0 + u < s1 ? z[a0 + u] : 0.0f;
+                }
+                // bits o .. o + 31 of the chunk's child mask, which may straddle two words
+                const int o = a0 - c0, wo = o >> 6, sh = o & 63;
+                uint64_t lo = km[0], hi = km[1];
+    #pragma unroll
+                for (int w = 1; w < 4; ++w)
+                    if (wo == w) {
+                        lo = km[w];
+                        hi = w + 1 < 4 ? km[w + 1] : 0;
+                    }
+                const uint32_t kb = (uint32_t)(sh == 0 ? lo : (lo >> sh) | (hi << (64 - sh)));
+    #pragma unroll
+                for (int u = 0; u < kRowBatch; ++u) {
+                    if (a0 + u < s1) {
+                        const double x = (double)zz[u] - (double)zmax;
+                        const double e = exp_nonpos_f64(unit_temp ? x : x / temp);
+                        fm += fixed_mass(e, fscale);
+                        if (!((kb >> u) & 1u)) s += e;
+                    }
+                }
+            }
+            // the pair's integer masses add exactly
+            const uint32_t flo = __shfl_xor((uint32_t)fm, 1, kWave), fhi = __shfl_xor((uint32_t)(fm >> 32), 1, kWave);
+            fm += ((uint64_t)fhi << 32) | flo;
+            if (half == 0) chunk_mass[((size_t)b * T + i) * kRowChunks + chunk] = fm;
+            s = block_sum_f64(s, s_red);
+            if (tid == 0) out->rest[q] = s;
+            // the same expression as the chunk masses' (x / 1 == x exactly), so the bonus
+            // draw can take a removed token's fixed-point mass out of its chunk exactly
+            if (q == 0 && tid < nk)
+                stats[(size_t)b * T + s_kid_row[tid]].e_kid =
+                    exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
+        }  // quarters
     }
-    if (q != 0) return;
+    if (q_first != 0) return;
     if (tid == 0) {
         out->zmax = zmax;
         out->argmax = amax;
@@ -480,10 +491,15 @@ hipError_t launch_verify(const eagle_tree_cfg& cfg, const float* target, const i
     const int T = cfg.n + 1;
     RowStats* stats = (RowStats*)workspace;
     uint64_t* chunk_mass = (uint64_t*)((unsigned char*)workspace + stats_bytes(cfg));
-    // rows padded to a multiple of 8 so the quarters of a row share an XCD
-    const int row_groups = (T + 7) / 8;
-    verify_rows_kernel<<<dim3(8 * kRowSplit * row_groups, cfg.batch), kRowThreads, 0, stream>>>(
-        target, T, cfg.vocab, flat_token, flat_parent, temperature, stats, chunk_mass);
+    if ((int64_t)cfg.batch * T >= kWholeRowsFrom) {
+        verify_rows_kernel<true><<<dim3(T, cfg.batch), kRowThreads, 0, stream>>>(
+            target, T, cfg.vocab, flat_token, flat_parent, temperature, stats, chunk_mass);
+    } else {
+        // rows padded to a multiple of 8 so the quarters of a row share an XCD
+        const int row_groups = (T + 7) / 8;
+        verify_rows_kernel<false><<<dim3(8 * kRowSplit * row_groups, cfg.batch), kRowThreads, 0, stream>>>(
+            target, T, cfg.vocab, flat_token, flat_parent, temperature, stats, chunk_mass);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     verify_walk_kernel<<<cfg.batch, kWalkThreads, 0, stream>>>(

@@ -412,6 +412,49 @@ def test_edge_cases(lib, orc, kw):
     verify_check(orc, vs, w, target, ft, fp, 0.9, 31, range(6))
 
 
+def test_verify_whole_row_mode_same_bits(lib):
+    """With many tree rows in a call (batch x T >= 256) one workgroup takes a whole
+    target row; with few, four workgroups split it.  Both must leave the same row
+    statistics and chunk masses, bit for bit: sequence b of a batch of 8 (whole
+    rows) against the same sequence verified alone (split rows), greedy and
+    sampled; the first sequence's outputs too (its uniforms are the same)."""
+    eb, stepm, wl = lib
+    w = small(wl, batch=8, ctx_range=(0, 100), n=60, depth=6, topk=10, m=10, vocab=5000, seed=41)
+    vs = stepm.VerifyStep(w)
+    vs.tree()
+    torch.cuda.synchronize()
+    B, T, V = w.batch, w.T, w.vocab
+    assert B * T >= 256 and T < 256
+    rng = np.random.default_rng(5)
+    vs.set_target(rng.normal(0.0, 2.0, size=(B, T, V)).astype(np.float32))
+    RS = 48  # sizeof(RowStats): four fp64 rest masses, the child's fp64 mass, zmax, argmax
+    stats_pad = lambda rows: (rows * RS + 255) // 256 * 256
+    cfg1 = eb.make_cfg(1, V, w.depth, w.topk, w.m, w.n)
+    ws1 = torch.zeros(eb.eagle_verify_workspace(cfg1), dtype=torch.uint8, device="cuda")
+    al1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ap1 = torch.zeros((1, w.depth), dtype=torch.int32, device="cuda")
+    ot1 = torch.zeros((1, w.depth + 1), dtype=torch.int32, device="cuda")
+    for temp in (0.0, 1.0, 0.7):
+        vs.verify(temp, 11, 3)
+        torch.cuda.synchronize()
+        full = vs.verify_ws.cpu().numpy()
+        chunks_full = full[stats_pad(B * T):stats_pad(B * T) + B * T * 1024 * 8]
+        for b in range(B):
+            eb.eagle_verify(cfg1, vs.target[b:b + 1], vs.flat_token[b:b + 1], vs.flat_parent[b:b + 1], temp, 11, 3,
+                            al1, ap1, ot1, ws1)
+            torch.cuda.synchronize()
+            one = ws1.cpu().numpy()
+            st_b = full[b * T * RS:(b + 1) * T * RS]
+            assert np.array_equal(st_b, one[:T * RS]), f"row statistics differ, sequence {b}, T = {temp}"
+            if temp > 0.0:
+                ch1 = one[stats_pad(T):stats_pad(T) + T * 1024 * 8]
+                assert np.array_equal(chunks_full[b * T * 8192:(b + 1) * T * 8192], ch1), \
+                    f"chunk masses differ, sequence {b}, T = {temp}"
+            if b == 0:
+                assert int(al1.item()) == int(vs.accept_len[0].item())
+                assert torch.equal(ap1[0], vs.accept_path[0]) and torch.equal(ot1[0], vs.out_tokens[0])
+
+
 def test_branch_independence_on_gpu(lib, orc):
     eb, stepm, wl = lib
     w = small(wl, n=12, ctx=90)
