@@ -73,10 +73,7 @@ constexpr int kD = 128;
 constexpr int kTileKeys = plan::kTileKeys;
 constexpr int kUnitRows = plan::kUnitRows;
 constexpr int kComputeWaves = 4;                     // 2 query halves x 2 key halves
-#ifndef EAGLE_LOADERS
-#define EAGLE_LOADERS 4
-#endif
-constexpr int kLoaders = EAGLE_LOADERS;              // waves that issue the loads
+constexpr int kLoaders = 4;                          // waves that issue the loads
 constexpr int kThreads = (kComputeWaves + kLoaders) * 64;
 constexpr int kStages = 4;
 constexpr int kGridWG = 256;                         // one per CU, multiple of the 8 XCDs
