@@ -910,7 +910,7 @@ __device__ __forceinline__ void tile_loop(const AttnArgs& a, const Tab& tab, uns
             }
         }
         if (!has_next) break;
-        sacc = snext;
+        if (!loader) sacc = snext;  // the loader waves never compute scores
         tc = tn;
         plan::advance(wn, tn.nkeys, tab, B, a.RG, UPS);
         mword_c = mword_n;
@@ -1239,7 +1239,7 @@ __global__ __launch_bounds__(kF32Waves * 64) void tree_attn_f32_kernel(AttnF32Ar
     const int ctx = a.ctx_len[b], S = ctx + a.T, D = a.D;
     const uint64_t mword = a.mask[(int64_t)b * a.T + i];
     const E* qrow = a.q + (((int64_t)b * a.T + i) * a.Hq + hq) * D;
-    if (threadIdx.x < D) s_q[threadIdx.x] = (float)qrow[threadIdx.x] * a.scale;
+    if ((int)threadIdx.x < D) s_q[threadIdx.x] = (float)qrow[threadIdx.x] * a.scale;
     __syncthreads();
     const int64_t base = ((int64_t)g * a.kv_rows_total + a.kv_row_off[b]) * D;
     float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;

@@ -243,7 +243,7 @@ EAGLE_HD inline int part_slot(int v, bool from0) { return 2 * v + (from0 ? 1 : 0
 // Returns false when there is none; otherwise the unit and its stretches vf = v ..
 // vl.  te = split_tile at stretch_start(v + 1).
 template <class Tab>
-EAGLE_HD inline bool split_unit_from(const Tab& tab, const Split& sp, int B, int UPS, int v, const Pos& te,
+EAGLE_HD inline bool split_unit_from(const Tab& tab, const Split& sp, int B, int /*UPS*/, int v, const Pos& te,
                                      int& b, int& uis, int& vl) {
     if (te.b >= B || te.tile == 0) return false;  // stretch v ends on a unit boundary (or the line's end)
     b = te.b;
