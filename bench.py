@@ -343,7 +343,7 @@ def main():
                          "known size whose FETCH_SIZE / WRITE_SIZE counters scale the attention's)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch

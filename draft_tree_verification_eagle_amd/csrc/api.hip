@@ -14,7 +14,7 @@ bool tree_cfg_ok(const eagle_tree_cfg* c) {
            c->topk >= 1 && c->m >= 1 && c->n >= 0 && c->topk <= c->vocab;
 }
 
-// Tree shape implied by the cfg; false if it exceeds this build's limits.
+// Tree shape implied by the cfg; false if it exceeds the library's limits.
 bool tree_shape(const eagle_tree_cfg* c, int32_t* capacity) {
     int64_t f = 1, cap = 1;
     for (int l = 0; l < c->depth; ++l) {
@@ -299,7 +299,7 @@ const char* eagle_status_string(int status) {
     switch (status) {
         case EAGLE_OK: return "ok";
         case EAGLE_ERR_INVALID_ARG: return "invalid argument";
-        case EAGLE_ERR_UNSUPPORTED: return "unsupported by this build";
+        case EAGLE_ERR_UNSUPPORTED: return "unsupported shape or type";
         case EAGLE_ERR_WORKSPACE: return "workspace missing or too small";
         case EAGLE_ERR_HIP: return "HIP launch error";
         default: return "unknown status";

@@ -58,14 +58,14 @@ extern "C" {
 typedef enum {
     EAGLE_OK = 0,
     EAGLE_ERR_INVALID_ARG = -1, /* null pointer, out-of-range size, inconsistent shape */
-    EAGLE_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits (below) */
+    EAGLE_ERR_UNSUPPORTED = -2, /* valid but outside the library's limits (below) */
     EAGLE_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required */
     EAGLE_ERR_HIP = -4          /* the HIP runtime reported a launch error */
 } eagle_status;
 
 typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define EAGLE_MAX_TREE_ROWS 64     /* T = n + 1: one 64-bit ancestor-mask word per row */
 #define EAGLE_MAX_TOPK 32          /* children per expanded node */
 #define EAGLE_MAX_LAYER_NODES 1024 /* m * topk: nodes created in one layer */

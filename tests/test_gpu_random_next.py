@@ -25,6 +25,12 @@ def draft_rows_every_layer(eb, stepm, orc, w):
             eb.eagle_tree_expand(vs.cfg, layer - 1, vs.draft_layers[layer - 2], vs.root, vs.state, vs.expand_ws)
         T_sub = eb.eagle_draft_subtree_rows(vs.cfg, layer)
         buf = N._subtree_buffers(w, T_sub)
+        if T_sub > 64:  # more rows than one mask word: documented as unsupported, nothing launched
+            with pytest.raises(eb.EagleError) as err:
+                eb.eagle_draft_subtree(vs.cfg, layer, vs.state, vs.ctx_len, buf["node"], buf["parent"],
+                                       buf["position"], buf["mask"], buf["query_row"])
+            assert err.value.status == eb.EAGLE_ERR_UNSUPPORTED
+            continue
         eb.eagle_draft_subtree(vs.cfg, layer, vs.state, vs.ctx_len, buf["node"], buf["parent"], buf["position"],
                                buf["mask"], buf["query_row"])
         torch.cuda.synchronize()
