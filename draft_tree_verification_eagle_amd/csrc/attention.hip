@@ -79,10 +79,8 @@ constexpr int kStages = 4;
 constexpr int kGridWG = 256;                         // one per CU, multiple of the 8 XCDs
 static_assert(kGridWG % 8 == 0, "workgroups are dealt to the 8 XCDs in turn");
 
-// Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
-// the XCDs in turn).  Of n stretches, XCD x takes [xcd_first(x, n),
-// xcd_first(x + 1, n)): one contiguous run each, sizes differing by at most one.
-__host__ __device__ inline int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
+using plan::xcd_first;
+using plan::xcd_of;
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kTileKeys * kRowBytes;    // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;          // K tile | V tile
@@ -1367,9 +1365,7 @@ int host_plan(HostPlan& hp, MergePlan& mp, Split& sp, const int32_t* ctx, const 
         int b, uis, vl;
         const Pos te = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, v + 1));
         if (!plan::split_unit_from(tab, sp, B, UPS, v, te, b, uis, vl)) continue;
-        const int mid = (v + vl) / 2;
-        int x = 0;
-        while (x < 7 && xcd_first(x + 1, sp.nwg) <= mid) ++x;
+        const int x = xcd_of((v + vl) / 2, sp.nwg);
         for (int rb = 0; rb < kRowBlocks; ++rb) {
             if (n_xcd[x] == kPlanWgs / 8) return -1;
             by_xcd[x][n_xcd[x]++] = (1ull << 63) | (uint64_t)(uint32_t)b | ((uint64_t)(uint32_t)uis << 16) |

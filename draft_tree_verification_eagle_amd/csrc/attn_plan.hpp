@@ -235,6 +235,19 @@ EAGLE_HD inline void advance(Walker& w, int nkeys, const Tab& tab, int B, int RG
     }
 }
 
+// Workgroup blk of a launch runs on XCD blk % 8 (the dispatcher deals workgroups
+// to the XCDs in turn).  Of n stretches, XCD x takes [xcd_first(x, n),
+// xcd_first(x + 1, n)): one contiguous run each, sizes differing by at most one;
+// workgroup blk takes stretch xcd_first(blk % 8, n) + blk / 8 when that lies in
+// its XCD's run.
+EAGLE_HD inline int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
+// The XCD whose run holds stretch v.
+EAGLE_HD inline int xcd_of(int v, int n) {
+    int x = 0;
+    while (x < 7 && xcd_first(x + 1, n) <= v) ++x;
+    return x;
+}
+
 // Partial slot of a piece (see above).
 EAGLE_HD inline int part_slot(int v, bool from0) { return 2 * v + (from0 ? 1 : 0); }
 

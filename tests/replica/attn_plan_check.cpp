@@ -17,7 +17,8 @@
 //     last (from0);
 //   * the workgroup -> stretch map (XCD runs) gives each stretch one workgroup;
 //   * every division the kernel takes from a host reciprocal (by the stretch count,
-//     by a sequence's unit cost, by RG and by T) equals the plain division.
+//     by a sequence's unit cost, by RG and by T) equals the plain division;
+//   * xcd_of names the XCD run of every stretch, as the merge plan uses it.
 // Input (stdin): grid T Hq Hkv rows_total B, then B pairs (ctx, row0).
 #define EAGLE_HD
 #include "../../draft_tree_verification_eagle_amd/csrc/attn_plan.hpp"
@@ -57,8 +58,6 @@ struct HostTab {
         return q;
     }
 };
-
-static int xcd_first(int x, int n) { return (x * n + 7) >> 3; }
 
 int main() {
     int grid, T, Hq, Hkv, B;
@@ -198,6 +197,10 @@ int main() {
         found[std::make_pair(b, uis)] = std::make_pair(v, vl);
     }
     CHECK(found == unit_range);
+    for (int v = 0; v < sp.nwg; ++v) {
+        const int x = xcd_of(v, sp.nwg);
+        CHECK(x == (owner[v] & 7) && v >= xcd_first(x, sp.nwg) && v < xcd_first(x + 1, sp.nwg));
+    }
     long long split_units = 0;
     for (int b = 0; b < B; ++b)
         for (int u = 0; u < UPS; ++u) {
