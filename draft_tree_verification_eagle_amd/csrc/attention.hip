@@ -17,8 +17,8 @@
 //    next, so short sequences share the GPU instead of each filling it alone.
 //    Workgroup index -> list position is XCD-aware (blockIdx % 8 picks the XCD):
 //    each XCD takes one contiguous run of stretches, so the units that share K/V
-//    rows (GQA) read them through one L2, and the partials of a unit land mostly
-//    in one L2.
+//    rows (GQA) read them through one L2, and most partials of a unit come from
+//    one XCD.
 //  * Eight waves per workgroup: four compute, four only load.  K and V stream HBM ->
 //    LDS by direct 16-byte global_load_lds (no register staging), four stages
 //    deep, issued and waited for by the loader waves alone (each issues a quarter
@@ -48,8 +48,9 @@
 //    fp16 (relative rounding 2^-11, inside the bf16 output's own).  The merge
 //    kernel, on the same stream, combines the partials of split units, so no
 //    workgroup ever waits for another; each unit is merged on the XCD whose
-//    stretches hold the middle of it, where most of its partials are still in
-//    L2 (written back, not dropped, when the main kernel ends).
+//    stretches hold the middle of it (measured faster than a merge indexed by
+//    unit alone, although the partials are mostly read from beyond L2, where the
+//    main kernel's end wrote them back).
 #include "attn_plan.hpp"
 #include "device_common.hpp"
 #include "launchers.hpp"
@@ -1031,9 +1032,8 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 // Merge: one workgroup per (split unit, 16 query rows); thread = (row, 8 dims).
 // The partials of the unit's pieces are combined kMergeBatch at a time, their
 // loads issued together.  With a host plan, workgroup blk runs on XCD blk % 8
-// and merges rows of a unit whose middle piece that XCD computed (most of its
-// partials are still in that XCD's L2); without one, workgroup (v, row block)
-// merges the split unit whose first stretch is v, if any.
+// and merges rows of a unit whose middle piece that XCD computed; without one,
+// workgroup (v, row block) merges the split unit whose first stretch is v, if any.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
 constexpr int kRowBlocks = kUnitRows / 16;
