@@ -171,6 +171,8 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     const float zmax = logit_key_value(best);
     const int nk = s_nk;
     RowStats* out = stats + (size_t)b * T + i;
+    // the children's logits, requested now so their latency overlaps the mass pass
+    const float z_kid = q_first == 0 && temperature > 0.0f && tid < nk ? z[s_kid_tok[tid]] : 0.0f;
     if (temperature > 0.0f) {
         const double temp = (double)temperature;
         const bool unit_temp = temperature == 1.0f;  // x / 1 == x: skip the fp64 divide
@@ -238,8 +240,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
             // the same expression as the chunk masses' (x / 1 == x exactly), so the bonus
             // draw can take a removed token's fixed-point mass out of its chunk exactly
             if (q == 0 && tid < nk)
-                stats[(size_t)b * T + s_kid_row[tid]].e_kid =
-                    exp_nonpos_f64(((double)z[s_kid_tok[tid]] - (double)zmax) / temp);
+                stats[(size_t)b * T + s_kid_row[tid]].e_kid = exp_nonpos_f64(((double)z_kid - (double)zmax) / temp);
         }  // quarters
     }
     if (q_first != 0) return;
