@@ -1036,12 +1036,10 @@ __global__ __launch_bounds__(kThreads, 1) void tree_attn_bf16_kernel(AttnArgs a)
 // workgroup (v, row block) merges the split unit whose first stretch is v, if any.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
-constexpr int kRowBlocks = kUnitRows / 16;
-constexpr int kPlanWgs = 256;  // merge workgroups a host plan covers (64 split units)
-// Per merge workgroup: bit 63 set = in use, then b (bits 0..15), uis (16..39), vf
-// (40..47), vl (48..55), row block (56..57); read by workgroup index alone.
+constexpr int kRowBlocks = plan::kMergeRowBlocks;
+// One entry per merge workgroup (attn_plan.hpp: merge_plan, merge_unpack).
 struct MergePlan {
-    uint64_t e[kPlanWgs];
+    uint64_t e[plan::kPlanWgs];
 };
 struct MergeArgs {
     __bf16* o;
@@ -1110,13 +1108,13 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(MergeArgs m) {
     }
     int b, uis, vf, vl, rb;
     if constexpr (kHostPlan) {
-        const uint64_t e = m.mp.e[blockIdx.x];
-        if (!(e >> 63)) return;
-        b = (int)(e & 0xFFFFu);
-        uis = (int)((e >> 16) & 0xFFFFFFu);
-        vf = (int)((e >> 40) & 0xFFu);
-        vl = (int)((e >> 48) & 0xFFu);
-        rb = (int)((e >> 56) & 3u);
+        plan::MergeEntry me;
+        if (!plan::merge_unpack(m.mp.e[blockIdx.x], me)) return;
+        b = me.b;
+        uis = me.uis;
+        vf = me.vf;
+        vl = me.vl;
+        rb = me.rb;
     } else {
         __shared__ int32_t s_S[plan::kMaxSeqs];
         __shared__ int64_t s_row0[plan::kMaxSeqs];
@@ -1359,25 +1357,7 @@ int host_plan(HostPlan& hp, MergePlan& mp, Split& sp, const int32_t* ctx, const 
     }
     const ArgTab tab{&hp};
     sp = plan::make_split_recip(hp.cost0[B], kGridWG, B * UPS);
-    uint64_t by_xcd[8][kPlanWgs];
-    int n_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int v = 0; v < sp.nwg; ++v) {
-        int b, uis, vl;
-        const Pos te = plan::split_tile(tab, B, UPS, plan::stretch_start(sp, v + 1));
-        if (!plan::split_unit_from(tab, sp, B, UPS, v, te, b, uis, vl)) continue;
-        const int x = xcd_of((v + vl) / 2, sp.nwg);
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            if (n_xcd[x] == kPlanWgs / 8) return -1;
-            by_xcd[x][n_xcd[x]++] = (1ull << 63) | (uint64_t)(uint32_t)b | ((uint64_t)(uint32_t)uis << 16) |
-                                    ((uint64_t)v << 40) | ((uint64_t)vl << 48) | ((uint64_t)rb << 56);
-        }
-    }
-    int most = 0;
-    for (int x = 0; x < 8; ++x) most = n_xcd[x] > most ? n_xcd[x] : most;
-    // workgroup blk = 8 j + x runs on XCD x and takes that XCD's j-th entry
-    for (int j = 0; j < most; ++j)
-        for (int x = 0; x < 8; ++x) mp.e[8 * j + x] = j < n_xcd[x] ? by_xcd[x][j] : 0;
-    return 8 * most;
+    return plan::merge_plan(tab, sp, B, UPS, mp.e);
 }
 
 }  // namespace

@@ -267,5 +267,57 @@ EAGLE_HD inline bool split_unit_from(const Tab& tab, const Split& sp, int B, int
     return true;
 }
 
+// Merge plan, built on the host when it has the context lengths: one 64-bit entry
+// per merge workgroup, read by workgroup index alone.  Bit 63 set = in use, then
+// sequence b (bits 0..15), unit uis (16..39), first and last stretch vf (40..47)
+// and vl (48..55), row block (56..57; a workgroup merges 16 of the unit's 64
+// rows).  Each split unit's row blocks go to the XCD whose run holds the unit's
+// middle stretch; workgroup 8 j + x runs on XCD x and takes that XCD's j-th entry.
+constexpr int kMergeRowBlocks = kUnitRows / 16;
+constexpr int kPlanWgs = 256;  // merge workgroups a plan covers (64 split units)
+struct MergeEntry {
+    int b, uis, vf, vl, rb;
+};
+EAGLE_HD inline uint64_t merge_pack(int b, int uis, int vf, int vl, int rb) {
+    return (1ull << 63) | (uint64_t)(uint32_t)b | ((uint64_t)(uint32_t)uis << 16) | ((uint64_t)(uint32_t)vf << 40) |
+           ((uint64_t)(uint32_t)vl << 48) | ((uint64_t)(uint32_t)rb << 56);
+}
+// False for an unused entry.
+EAGLE_HD inline bool merge_unpack(uint64_t e, MergeEntry& m) {
+    if (!(e >> 63)) return false;
+    m.b = (int)(e & 0xFFFFu);
+    m.uis = (int)((e >> 16) & 0xFFFFFFu);
+    m.vf = (int)((e >> 40) & 0xFFu);
+    m.vl = (int)((e >> 48) & 0xFFu);
+    m.rb = (int)((e >> 56) & 3u);
+    return true;
+}
+// Fills e[0 .. kPlanWgs) (unused entries 0) and returns the merge workgroups to
+// launch (8 x the most entries any XCD has), or -1 when an XCD would need more
+// than kPlanWgs / 8 entries or a field would not fit (B <= 2^16, UPS <= 2^24 and
+// nwg <= 256 always fit).  Host side.
+template <class Tab>
+inline int merge_plan(const Tab& tab, const Split& sp, int B, int UPS, uint64_t* e) {
+    if (B > (1 << 16) || UPS > (1 << 24) || sp.nwg > 256) return -1;
+    uint64_t by_xcd[8][kPlanWgs / 8];
+    int n_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int v = 0; v < sp.nwg; ++v) {
+        int b, uis, vl;
+        const Pos te = split_tile(tab, B, UPS, stretch_start(sp, v + 1));
+        if (!split_unit_from(tab, sp, B, UPS, v, te, b, uis, vl)) continue;
+        const int x = xcd_of((v + vl) / 2, sp.nwg);
+        for (int rb = 0; rb < kMergeRowBlocks; ++rb) {
+            if (n_xcd[x] == kPlanWgs / 8) return -1;
+            by_xcd[x][n_xcd[x]++] = merge_pack(b, uis, v, vl, rb);
+        }
+    }
+    int most = 0;
+    for (int x = 0; x < 8; ++x) most = n_xcd[x] > most ? n_xcd[x] : most;
+    for (int k = 0; k < kPlanWgs; ++k) e[k] = 0;
+    for (int j = 0; j < most; ++j)
+        for (int x = 0; x < 8; ++x) e[8 * j + x] = j < n_xcd[x] ? by_xcd[x][j] : 0;
+    return 8 * most;
+}
+
 }  // namespace plan
 }  // namespace eagle

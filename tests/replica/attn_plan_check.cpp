@@ -18,7 +18,11 @@
 //   * the workgroup -> stretch map (XCD runs) gives each stretch one workgroup;
 //   * every division the kernel takes from a host reciprocal (by the stretch count,
 //     by a sequence's unit cost, by RG and by T) equals the plain division;
-//   * xcd_of names the XCD run of every stretch, as the merge plan uses it.
+//   * xcd_of names the XCD run of every stretch, as the merge plan uses it;
+//   * the host's merge plan (merge_plan): every split unit's four row blocks exactly
+//     once, with its sequence, unit, vf and vl, each on the XCD whose run holds the
+//     unit's middle stretch (entry k runs on XCD k % 8), the unused entries empty,
+//     and -1 exactly when an XCD would need more than kPlanWgs / 8 entries.
 // Input (stdin): grid T Hq Hkv rows_total B, then B pairs (ctx, row0).
 #define EAGLE_HD
 #include "../../draft_tree_verification_eagle_amd/csrc/attn_plan.hpp"
@@ -200,6 +204,38 @@ int main() {
     for (int v = 0; v < sp.nwg; ++v) {
         const int x = xcd_of(v, sp.nwg);
         CHECK(x == (owner[v] & 7) && v >= xcd_first(x, sp.nwg) && v < xcd_first(x + 1, sp.nwg));
+    }
+    // the host's merge plan
+    {
+        std::vector<uint64_t> e(kPlanWgs, ~0ull);
+        const int r = merge_plan(tab, sp, B, UPS, e.data());
+        int per_xcd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (const auto& u : found) per_xcd[xcd_of((u.second.first + u.second.second) / 2, sp.nwg)] += kMergeRowBlocks;
+        int most = 0;
+        for (int x = 0; x < 8; ++x) most = per_xcd[x] > most ? per_xcd[x] : most;
+        if (most > kPlanWgs / 8) {
+            CHECK(r == -1);
+        } else {
+            CHECK(r == 8 * most);
+            std::map<std::pair<int, int>, int> blocks;  // (b, uis) -> bit mask of row blocks
+            for (int k = 0; k < kPlanWgs; ++k) {
+                MergeEntry m;
+                if (!merge_unpack(e[k], m)) {
+                    CHECK(e[k] == 0);
+                    continue;
+                }
+                CHECK(k < r);
+                auto it = found.find(std::make_pair(m.b, m.uis));
+                CHECK(it != found.end() && it->second == std::make_pair(m.vf, m.vl));
+                CHECK(xcd_of((m.vf + m.vl) / 2, sp.nwg) == k % 8);
+                CHECK(m.rb >= 0 && m.rb < kMergeRowBlocks);
+                int& bits = blocks[std::make_pair(m.b, m.uis)];
+                CHECK(!((bits >> m.rb) & 1));
+                bits |= 1 << m.rb;
+            }
+            CHECK(blocks.size() == found.size());
+            for (const auto& bl : blocks) CHECK(bl.second == (1 << kMergeRowBlocks) - 1);
+        }
     }
     long long split_units = 0;
     for (int b = 0; b < B; ++b)
