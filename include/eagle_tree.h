@@ -36,7 +36,8 @@
  *   - All array pointers are DEVICE pointers owned by the caller; struct
  *     arguments (eagle_tree_cfg, eagle_tree_state, eagle_attn_desc) are read on the
  *     host during the call only.  The library never allocates or frees device
- *     memory and keeps no state between calls.
+ *     memory and keeps no state between calls, except the one file-scope scratch
+ *     array (and its per-device address) of eagle_tree_attention_noalloc.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
  *   - Arguments are validated on the host first; on any failure the call returns
  *     the status and launches nothing.  After launching, a launch error maps to
