@@ -115,7 +115,7 @@ def _cpu_all_cores(w, mask, t_tree, t_verify):
                       f"threads capped at the {HOST_THREAD_SHARE}-thread host share of one GPU"}
 
 
-def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 8):
+def cpu_baseline(w, vs_draft, vs_root, target, temperature, seed, layers: int = 12):
     """Oracle timing on a bounded sample: full tree + `layers` distinct attention
     layers + one verification, single-threaded, scaled to the full step
     (tree + w.layers x mean layer time + verify)."""
