@@ -20,7 +20,7 @@ The JSON line carries:
             main kernel and its partial-merge kernel.  `traffic` (HBM bytes per
             launch from FETCH_SIZE / WRITE_SIZE counters, scaled by a copy of known
             size) is read from the committed counter summary when present.
-  cpu_baseline  the CPU oracle on a bounded sample (tree + 8 attention layers +
+  cpu_baseline  the CPU oracle on a bounded sample (tree + 12 attention layers +
             verify, single thread, about 10 s), scaled to one full step
 """
 from __future__ import annotations
