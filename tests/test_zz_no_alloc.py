@@ -80,3 +80,33 @@ def test_noalloc_size_limit_and_bad_arguments(lib):
     assert L.eagle_tree_attention_noalloc(C.byref(d2), None, f, f, f, f, None, None) == eb.EAGLE_ERR_INVALID_ARG
     d3 = eb.make_attn_desc(eb.EAGLE_BF16, 1, 16, 8, 8, 130, dev, dev, 4096)  # head_dim > 128: rejected
     assert L.eagle_tree_attention_noalloc(C.byref(d3), f, f, f, f, f, None, None) == eb.EAGLE_ERR_UNSUPPORTED
+
+
+def test_noalloc_graph_replays_match_eager(lib):
+    """The callers this entry point is for include code under HIP graph capture: a
+    captured no-alloc call replays to its eager result bit for bit, with eager
+    no-alloc calls on other inputs (which overwrite the shared array) in between."""
+    eb, stepm, wl = lib
+    w = shape(wl, batch=2, ctx_range=(700, 3000), n_q_heads=16, n_kv_heads=4, n=40, depth=5, topk=8, m=8, seed=58)
+    other = shape(wl, batch=1, ctx=5000, n_q_heads=40, n_kv_heads=40, n=60, depth=6, topk=10, m=10, seed=59)
+    say(f"[no-alloc graph] batch {w.batch}, heads {w.n_q_heads}/{w.n_kv_heads}, T {w.T}")
+    vs = stepm.VerifyStep(w)
+    vs.tree()
+    vo = stepm.VerifyStep(other)
+    vo.tree()
+    a, ao = vs.attn[0], vo.attn[0]
+    o = torch.empty_like(a["o"]); lse = torch.empty_like(a["lse"])
+    eb.eagle_tree_attention_noalloc(vs.desc, a["q"], a["k"], a["v"], vs.mask, o, lse)  # eager, also the warm-up
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eb.eagle_tree_attention_noalloc(vs.desc, a["q"], a["k"], a["v"], vs.mask, o, lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        eb.eagle_tree_attention_noalloc(vo.desc, ao["q"], ao["k"], ao["v"], vo.mask, ao["o"], ao["lse"])
+        o.fill_(7.0); lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep} differs from the eager call"
