@@ -123,6 +123,13 @@ CONFIGS = {
                             n_q_heads=40, n_kv_heads=40, head_dim=128, layers=40, batch=16,
                             ctx=0, ctx_range=(512, 16384), dtype="bf16", draft_sigma=3.0,
                             target_sigma=2.0, temperatures=(1.0,), plant_frac=0.5, seed=1005),
+    # The largest batch the library takes: 1024 sequences, each a small tree (T = 9) over
+    # a short context (0-60 tokens), one layer of 4 heads (four attention launches of
+    # 256 sequences).
+    "batch1024_small": Workload("batch1024_small", vocab=300, depth=3, topk=3, m=2, n=8,
+                                n_q_heads=4, n_kv_heads=4, head_dim=128, layers=1, batch=1024,
+                                ctx=0, ctx_range=(0, 60), dtype="bf16", draft_sigma=2.0,
+                                target_sigma=2.0, temperatures=(0.0,), plant_frac=0.5, seed=1006),
 }
 CONFIG_ORDER = ["tiny_f32", "llama2_7b_layer", "llama2_13b", "llama2_70b_gqa", "batched_13b"]
 
